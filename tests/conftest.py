@@ -1,0 +1,19 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size case (minutes of host time)")
+
+
+def pytest_collection_modifyitems(config, items):
+    # a GPU test on a machine without a GPU is a configuration error, not a skip:
+    # the driver runs `-m gpu` only on the GPU machine.
+    pass
