@@ -1,0 +1,236 @@
+"""Benchmark of one replay step on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic member: build the
+prompt's page table (host split + upload), the split forward over the paged
+prompt, the causal response block, the exact LSE merge, and the
+response-only backward (D = rowsum(dO*O), per-split dQ, response dQ, response
+dK/dV, ordered dQ sum).  Inputs are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step
+(only unmasked scores counted: 4d flops per (head,row,key) forward; 6d per
+prompt key and 10d per response key backward, no prompt dK/dV work); the same
+line carries prompt-keys/s, the roofline of the dominant kernel (measured with
+HIP events on its launch stream over the timed region) and the float64 oracle
+timed on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
+DOMINANT = "bwd_prompt_dq"  # 60% of the algorithmic flops
+KERNELS = ("fwd_prompt", "fwd_combine", "fwd_resp", "lse_merge", "bwd_dot", "bwd_prompt_dq",
+           "bwd_resp_dq", "bwd_resp_dkdv", "dq_reduce")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_prompt_dq_traffic_prefix2M.md")
+
+
+def flops(shape) -> dict:
+    d, hq, r, p = shape.head_dim, shape.hq, shape.resp_len, shape.prompt_len
+    causal = r * (r + 1) // 2
+    return {
+        "fwd_prompt": 4 * d * hq * r * p,
+        "fwd_resp": 4 * d * hq * causal,
+        "bwd_prompt_dq": 6 * d * hq * r * p,
+        "bwd_resp": 10 * d * hq * causal,
+    }
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "response_replay_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(digest: str):
+    """Per-launch HBM bytes of the dominant kernel from the committed counter
+    summary, or None if it is missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shape, inp, seconds_hint: float = 20.0):
+    """The float64 oracle on the host, on a bounded sample: KV head 0, its
+    query heads, `rows` response rows each (always including the last rows,
+    whose causal response block is the largest)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from replay_inputs import logical_prompt
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    g = shape.hq // shape.hkv
+    # about 20 s of host work: ~2e6 (row x prompt-key) pairs per second measured
+    rows = max(1, min(16, shape.resp_len, (8 << 20) // max(shape.prompt_len, 1)))
+    t0 = time.perf_counter()
+    kp = logical_prompt(inp["k_pool"], inp["l2p"], shape.prompt_len, kv_heads=[0]).cpu()
+    vp = logical_prompt(inp["v_pool"], inp["l2p"], shape.prompt_len, kv_heads=[0]).cpu()
+    q = inp["q"][:g].cpu()
+    do = inp["d_o"][:g].cpu()
+    kr, vr = inp["k_resp"][:1].cpu(), inp["v_resp"][:1].cpu()
+    R = shape.resp_len
+    sel = np.tile(np.arange(R - rows, R), (g, 1))
+    t1 = time.perf_counter()
+    oracle.replay_forward(q, kp, vp, kr, vr, shape.scale, rows=sel)
+    oracle.replay_backward(q, kp, vp, kr, vr, do, shape.scale, rows=sel)
+    t2 = time.perf_counter()
+    d, P = shape.head_dim, shape.prompt_len
+    n = g * rows
+    resp_keys = sum(i + 1 for i in range(R - rows, R)) * g
+    algo = (4 + 6) * d * n * P + (4 + 10) * d * resp_keys
+    secs = t2 - t1
+    return {
+        "value": algo / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 oracle forward+backward of {n} response rows (KV head 0: {g} query heads x "
+                   f"the last {rows} rows) over the full {P}-position prompt; {secs:.1f} s compute "
+                   f"(+{t1 - t0:.1f} s to gather inputs), scaled as algorithmic flops per second"),
+        "prompt_keys_per_s_equiv": P * n / (shape.hq * R) / secs,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefix_24x4_d256_p2097152_r1024_s8")
+    ap.add_argument("--seed", type=int, default=20260002)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md for how the splits would shard over CP ranks); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from replay_inputs import WORKLOADS, make_inputs
+    from response_replay_attention_amd import (PromptCache, ls_timing_enable, ls_timing_read,
+                                               ls_timing_reset, replay_backward, replay_forward)
+
+    shape = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(shape, args.seed, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        cache = PromptCache(inp["k_pool"], inp["v_pool"], shape.prompt_len, inp["l2p"],
+                            shape.num_splits, shape.policy, shape.block_pages)
+        fwd = replay_forward(cache, inp["q"], inp["k_resp"], inp["v_resp"], shape.scale)
+        replay_backward(cache, inp["q"], inp["k_resp"], inp["v_resp"], fwd.o, fwd.lse,
+                        inp["d_o"], shape.scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ls_timing_reset()
+    ls_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ls_timing_enable(False)
+    kern = {}
+    for k in KERNELS:
+        n, ms = ls_timing_read(k)
+        if n:
+            kern[k] = {"launches": n, "avg_ms": ms / n}
+
+    f = flops(shape)
+    step_flops = sum(f.values())
+    ms_step = elapsed / args.steps * 1e3
+    tflops = step_flops * args.steps / elapsed / 1e12
+    dom = kern.get(DOMINANT, {"avg_ms": float("nan")})
+    achieved = f["bwd_prompt_dq"] / (dom["avg_ms"] * 1e-3) / 1e12
+    digest = source_digest()
+    traffic = read_traffic(digest)
+
+    out = {
+        "metric": "replay-attn fwd+bwd TFLOP/s & prompt-keys/s at 2M prefix; % bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": shape.name,
+            "q_heads": shape.hq, "kv_heads": shape.hkv, "head_dim": shape.head_dim,
+            "prompt_len": shape.prompt_len, "resp_len": shape.resp_len,
+            "splits": shape.num_splits, "page_size": shape.page_size,
+            "parallelism": "1 GPU; CP ranks emulated as page splits",
+        },
+        "prompt_keys_per_s": round(shape.prompt_len * args.steps / elapsed, 1),
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "kernel": DOMINANT,
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "source_digest": digest,
+        },
+        "kernels_avg_ms": {k: round(v["avg_ms"], 4) for k, v in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,224 @@
+/*
+ * ls_replay.h -- C ABI of the response-replay attention library (MI355X, gfx950).
+ *
+ * The operator: exact attention of one short response branch (R rows, causal
+ * within the response) over a long, detached prompt whose K/V live in fixed
+ * size pages, for a grouped-query attention layer (Hq query heads sharing Hkv
+ * K/V heads).  This is the full-attention layer of the LongStraw "Qwen path":
+ * compact prompt K/V pages owned by context-parallel ranks, a global
+ * log-sum-exp merge of the per-rank partial attention, and a response-only
+ * backward that all-reduces only the query gradient (LongStraw review page,
+ * section 2 "core method", items 2-3, and the section 7 mind map,
+ * "Qwen3.6-27B implementation"; LongStraw abstract on cortexa.online: exact
+ * attention composition, response-only objective, detached prompt state).
+ *
+ * On one GPU each context-parallel rank is emulated by a "split": a list of
+ * prompt pages.  The forward writes one partial (max-shift m, sum-exp l,
+ * normalised output o) per split plus one for the causal response block;
+ * ls_lse_merge composes them exactly.  The backward returns dQ (over prompt and
+ * response keys, summed over splits in a fixed order) and dK/dV for the
+ * response keys only.  No prompt K/V gradient exists anywhere in this API: the
+ * prompt state is stopgrad (DeepRead summary page, "Method").
+ *
+ * Conventions for every call
+ *   - Pointers marked "device" are HIP device pointers; "host" are CPU memory.
+ *   - The caller allocates and owns every buffer, including workspaces.  The
+ *     library allocates no device memory and keeps no pointer after a call
+ *     returns.  Prompt pools are read-only: nothing ever writes them.
+ *   - Device pointers must be 16-byte aligned; tensors are dense row-major in
+ *     the layouts stated below.  bf16 = IEEE bfloat16 (1-8-7).
+ *   - GPU work is enqueued asynchronously on `stream` (0 = null stream).  A
+ *     device fault surfaces at the caller's next synchronisation.
+ *   - All argument checks happen before any HIP call, so a call that returns
+ *     an error has enqueued nothing.
+ *   - Supported: head_dim in {128, 256}; page_size == 256; Hq % Hkv == 0;
+ *     resp_len >= 1; prompt_len >= 0; Hq*resp_len*head_dim < 2^31.
+ */
+#ifndef LS_REPLAY_H
+#define LS_REPLAY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ls_status {
+  LS_OK = 0,
+  LS_ERR_INVALID_ARG = -1, /* null pointer, bad count, misaligned pointer     */
+  LS_ERR_UNSUPPORTED = -2, /* head_dim / page_size / shape this build lacks  */
+  LS_ERR_PAGE_RANGE = -3,  /* page id out of range or physical page reused   */
+  LS_ERR_WORKSPACE = -4,   /* workspace smaller than the size query returned */
+  LS_ERR_HIP = -5          /* a HIP launch or runtime call failed            */
+} ls_status;
+
+/* Page-split policies for ls_kv_page_table (one split = one emulated
+ * context-parallel rank). */
+enum {
+  LS_SPLIT_CONTIGUOUS = 0,  /* S consecutive page ranges, sizes differ by <= 1, longer first */
+  LS_SPLIT_BLOCK_CYCLIC = 1,/* logical page p -> split (p / block_pages) % S (the pages' CP8 rule) */
+  LS_SPLIT_EXPLICIT = 2     /* logical page p -> split owner[p] */
+};
+
+/* Shape of one replay-attention call.
+ *   num_q_heads  Hq;  num_kv_heads Hkv, Hq % Hkv == 0; query head h reads
+ *                K/V head h / (Hq/Hkv) (contiguous GQA groups).
+ *   head_dim     d in {128, 256}.
+ *   page_size    prompt tokens per page; must be 256.
+ *   prompt_len   P >= 0 prompt positions; all are visible to every response row.
+ *   resp_len     R >= 1 response rows; row i sees response keys 0..i.
+ *   scale        softmax scale applied to q.k (normally 1/sqrt(d)). */
+typedef struct ls_attn_shape {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int64_t prompt_len;
+  int32_t resp_len;
+  float scale;
+} ls_attn_shape;
+
+/* Page table of one prompt, as built by ls_kv_page_table and copied to the
+ * device by the caller.
+ *   l2p                 device int32 [num_pages]: logical page -> physical slot
+ *                       in the pools (slots in [0, num_phys_pages), no repeats).
+ *   order               device int32 [num_pages]: logical page ids, split-major.
+ *   split_offsets       device int32 [num_splits + 1]: CSR offsets into order.
+ *   split_offsets_host  host copy of split_offsets (used to size the launch).
+ * Logical page p holds prompt positions [p*page_size, (p+1)*page_size); only
+ * the last page may be partial (positions >= prompt_len are masked).  A page
+ * id outside its range seen by a kernel is skipped (treated as empty), so a
+ * corrupted device table gives wrong numbers, never an out-of-bounds read. */
+typedef struct ls_page_table {
+  const int32_t* l2p;
+  const int32_t* order;
+  const int32_t* split_offsets;
+  const int32_t* split_offsets_host;
+  int32_t num_pages;
+  int32_t num_splits;
+  int32_t num_phys_pages;
+} ls_page_table;
+
+/* Text for a status code (static storage; never NULL). */
+const char* ls_status_string(ls_status status);
+
+/* Library ABI version (major*100 + minor). */
+int32_t ls_version(void);
+
+/* ls_kv_page_table -- host only, pure (no HIP call).
+ * Validates the logical->physical page map of one prompt and deals its pages
+ * to num_splits splits (emulated context-parallel ranks; LongStraw review page,
+ * section 7 mind map: CP8 page ownership, block-cyclic).  Inside a split pages
+ * are listed in increasing logical order.
+ *   num_pages           >= 0, must equal ceil(prompt_len / page_size).
+ *   page_size           256.
+ *   logical_to_physical host [num_pages] or NULL (= identity, then
+ *                       num_phys_pages >= num_pages).
+ *   num_phys_pages      pool slots; every map entry must lie in [0, num_phys_pages)
+ *                       and no slot may appear twice (a compact page is its own
+ *                       allocation, never a view shared with another page).
+ *   num_splits          >= 1.
+ *   policy              LS_SPLIT_*; block_pages >= 1 is used by BLOCK_CYCLIC;
+ *                       owner (host [num_pages], values in [0, num_splits)) by
+ *                       EXPLICIT, else ignored (may be NULL).
+ *   order_out           host [num_pages]    (written on success).
+ *   split_offsets_out   host [num_splits+1] (written on success).
+ * Errors: LS_ERR_INVALID_ARG (counts, NULL outputs, prompt_len inconsistent
+ * with num_pages, unknown policy, bad owner), LS_ERR_UNSUPPORTED (page_size),
+ * LS_ERR_PAGE_RANGE (map entry out of range or repeated).  Splits may be empty. */
+ls_status ls_kv_page_table(int32_t num_pages, int32_t page_size, int64_t prompt_len,
+                           const int32_t* logical_to_physical, int32_t num_phys_pages,
+                           int32_t num_splits, int32_t policy, int32_t block_pages,
+                           const int32_t* owner, int32_t* order_out,
+                           int32_t* split_offsets_out);
+
+/* Workspace bytes the forward / backward need for this shape and table
+ * (0 on invalid arguments).  Pure host functions. */
+size_t ls_replay_attn_fwd_workspace(const ls_attn_shape* shape, const ls_page_table* pt);
+size_t ls_replay_attn_bwd_workspace(const ls_attn_shape* shape, const ls_page_table* pt);
+
+/* ls_replay_attn_fwd -- per-split partial attention (the forward of one
+ * replayed response; LongStraw review page, section 7 mind map: forward
+ * composition by global LSE over CP ranks).
+ * For every row (h, i) (row index h*R + i) and every part c in [0, S]:
+ *   parts c < S   cover the prompt pages of split c (all positions visible);
+ *   part  c == S  covers the response keys j <= i (causal, diagonal included).
+ *   x_j = scale * <q[h,i], k_j>;  part_m[c,row] = m, part_l[c,row] = sum_j exp(x_j - m),
+ *   part_o[c,row,:] = sum_j exp(x_j - m) v_j / part_l[c,row].
+ * m is a shift chosen by the kernel (within a few units of max_j x_j, never
+ * below it by more than 8*ln2); the pair (m, l) is what is defined: m + ln l is
+ * the split's log-sum-exp.  An empty split gives m = -inf, l = 0, o = 0.
+ *   q                 device bf16 [Hq, R, d]
+ *   k_pool, v_pool    device bf16 [num_phys_pages, Hkv, page_size, d]
+ *   k_resp, v_resp    device bf16 [Hkv, R, d]
+ *   part_o            device fp32 [S+1, Hq, R, d]
+ *   part_m, part_l    device fp32 [S+1, Hq, R]
+ *   workspace         device, >= ls_replay_attn_fwd_workspace() bytes (may be
+ *                     NULL when that is 0).
+ * Errors: LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP. */
+ls_status ls_replay_attn_fwd(const ls_attn_shape* shape, const ls_page_table* pt,
+                             const void* q, const void* k_pool, const void* v_pool,
+                             const void* k_resp, const void* v_resp,
+                             float* part_o, float* part_m, float* part_l,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ls_lse_merge -- exact composition of partial attention (the pages' global
+ * LSE/output merge of the CP8 shards; LongStraw review page, section 7 mind map).
+ * For each row: M = max_c m_c, w_c = l_c * exp(m_c - M), L = sum_c w_c,
+ *   o[row,:] = bf16_rne( sum_c w_c * part_o[c,row,:] / L ),  lse[row] = M + ln L.
+ * Parts are combined in index order; the result does not depend on how the
+ * keys were partitioned.  A row with L == 0 gets o = 0, lse = -inf.
+ *   num_parts >= 1; rows >= 1; head_dim in {128, 256}
+ *   part_o  device fp32 [num_parts, rows, head_dim]; part_m, part_l [num_parts, rows]
+ *   o_bf16  device bf16 [rows, head_dim];  lse device fp32 [rows] (natural log).
+ * Errors: LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_HIP. */
+ls_status ls_lse_merge(int32_t num_parts, int64_t rows, int32_t head_dim,
+                       const float* part_o, const float* part_m, const float* part_l,
+                       void* o_bf16, float* lse, hipStream_t stream);
+
+/* ls_replay_attn_bwd -- response-only backward of the replayed response.
+ * With P = exp(x - lse) recomputed from the saved natural-log lse and
+ * D = <dO, O> over the stored bf16 O:
+ *   dq[h,i,:]      = scale * sum_j P_ij (<dO_i, v_j> - D_i) k_j   over prompt AND
+ *                    response keys; the per-split terms are summed in split
+ *                    order, the response term last (this replaces the pages'
+ *                    dQ all-reduce across CP ranks; LongStraw review page,
+ *                    section 2: only the query gradient is all-reduced);
+ *   dk_resp[kv,j,:] = scale * sum_{h in group kv} sum_{i >= j} dS_ij q[h,i,:]
+ *   dv_resp[kv,j,:] =         sum_{h in group kv} sum_{i >= j} P_ij  dO[h,i,:]
+ * No gradient of the prompt K/V is formed (stopgrad; DeepRead summary,
+ * "Method"), and the pools are never written.
+ *   q, d_o, o      device bf16 [Hq, R, d] (o as written by ls_lse_merge)
+ *   lse            device fp32 [Hq, R]
+ *   k_pool, v_pool, k_resp, v_resp as in the forward
+ *   dq             device fp32 [Hq, R, d]
+ *   dk_resp, dv_resp device fp32 [Hkv, R, d]
+ *   workspace      device, >= ls_replay_attn_bwd_workspace() bytes.
+ * Errors: LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP. */
+ls_status ls_replay_attn_bwd(const ls_attn_shape* shape, const ls_page_table* pt,
+                             const void* q, const void* k_pool, const void* v_pool,
+                             const void* k_resp, const void* v_resp,
+                             const void* o, const float* lse, const void* d_o,
+                             float* dq, float* dk_resp, float* dv_resp,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Kernel timing (measurement aid).  While enabled, every kernel the library
+ * launches is bracketed by a pair of hipEvents recorded on the launch stream.
+ * ls_timing_read synchronises those events and returns, for the named kernel,
+ * the number of launches and their summed duration since the last reset.
+ * Kernel names: "fwd_prompt", "fwd_resp", "fwd_combine", "lse_merge",
+ * "bwd_dot", "bwd_prompt_dq", "bwd_resp_dq", "bwd_resp_dkdv", "dq_reduce".
+ * ls_timing_enable(0) stops recording; ls_timing_reset drops all records.
+ * Not thread-safe; calls overlapping on several host threads race. */
+ls_status ls_timing_enable(int32_t on);
+ls_status ls_timing_reset(void);
+ls_status ls_timing_read(const char* kernel, int32_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LS_REPLAY_H */

@@ -1,0 +1,211 @@
+"""Thin Python binding of libls_replay.so (include/ls_replay.h).
+
+Argument marshalling only: every step of the replay path runs in the HIP
+library.  PyTorch provides device memory and the stream.  The functions carry
+the C names and raise :class:`LsError` on a non-zero status.  There is no
+fallback: if the library is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libls_replay.so")
+
+LS_OK = 0
+LS_SPLIT_CONTIGUOUS = 0
+LS_SPLIT_BLOCK_CYCLIC = 1
+LS_SPLIT_EXPLICIT = 2
+PAGE_SIZE = 256
+
+# every symbol include/ls_replay.h declares
+EXPORTS = (
+    "ls_status_string", "ls_version", "ls_kv_page_table",
+    "ls_replay_attn_fwd_workspace", "ls_replay_attn_bwd_workspace",
+    "ls_replay_attn_fwd", "ls_lse_merge", "ls_replay_attn_bwd",
+    "ls_timing_enable", "ls_timing_reset", "ls_timing_read",
+)
+
+
+class LsError(RuntimeError):
+    def __init__(self, func: str, status: int, text: str):
+        super().__init__(f"{func} failed: status {status} ({text})")
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("prompt_len", ctypes.c_int64),
+        ("resp_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class PageTable(ctypes.Structure):
+    _fields_ = [
+        ("l2p", ctypes.c_void_p),
+        ("order", ctypes.c_void_p),
+        ("split_offsets", ctypes.c_void_p),
+        ("split_offsets_host", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32),
+    ]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m response_replay_attention_amd.build`")
+    h = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "ls_status_string": (ctypes.c_char_p, [I32]),
+        "ls_version": (I32, []),
+        "ls_kv_page_table": (I32, [I32, I32, I64, P, I32, I32, I32, I32, P, P, P]),
+        "ls_replay_attn_fwd_workspace": (SZ, [P, P]),
+        "ls_replay_attn_bwd_workspace": (SZ, [P, P]),
+        "ls_replay_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "ls_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P, P]),
+        "ls_replay_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "ls_timing_enable": (I32, [I32]),
+        "ls_timing_reset": (I32, []),
+        "ls_timing_read": (I32, [ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_double)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(h, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib_handle = h
+    return h
+
+
+def _check(func: str, status: int) -> None:
+    if status != LS_OK:
+        text = lib().ls_status_string(status).decode()
+        raise LsError(func, status, text)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: str = "") -> int:
+    if t is None:
+        return 0
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_shape(hq: int, hkv: int, head_dim: int, prompt_len: int, resp_len: int,
+               scale: float, page_size: int = PAGE_SIZE) -> AttnShape:
+    return AttnShape(hq, hkv, head_dim, page_size, prompt_len, resp_len, scale)
+
+
+# ----------------------------------------------------------------- C calls
+
+def ls_version() -> int:
+    return int(lib().ls_version())
+
+
+def ls_status_string(status: int) -> str:
+    return lib().ls_status_string(status).decode()
+
+
+def ls_kv_page_table(num_pages: int, page_size: int, prompt_len: int, l2p, num_phys_pages: int,
+                     num_splits: int, policy: int, block_pages: int = 1,
+                     owner=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Host page split.  ``l2p``/``owner``: int32 sequences or None.
+    Returns ``(order [num_pages], split_offsets [num_splits+1])`` (int32)."""
+    l2p_a = None if l2p is None else np.ascontiguousarray(np.asarray(l2p, dtype=np.int32))
+    own_a = None if owner is None else np.ascontiguousarray(np.asarray(owner, dtype=np.int32))
+    order = np.zeros(max(num_pages, 1), dtype=np.int32)
+    offs = np.zeros(max(num_splits, 0) + 1, dtype=np.int32)
+    st = lib().ls_kv_page_table(
+        num_pages, page_size, prompt_len,
+        None if l2p_a is None else l2p_a.ctypes.data, num_phys_pages, num_splits, policy,
+        block_pages, None if own_a is None else own_a.ctypes.data,
+        order.ctypes.data, offs.ctypes.data)
+    _check("ls_kv_page_table", st)
+    return order[:num_pages], offs
+
+
+def ls_replay_attn_fwd_workspace(shape: AttnShape, pt: PageTable) -> int:
+    return int(lib().ls_replay_attn_fwd_workspace(ctypes.byref(shape), ctypes.byref(pt)))
+
+
+def ls_replay_attn_bwd_workspace(shape: AttnShape, pt: PageTable) -> int:
+    return int(lib().ls_replay_attn_bwd_workspace(ctypes.byref(shape), ctypes.byref(pt)))
+
+
+def ls_replay_attn_fwd(shape: AttnShape, pt: PageTable, q, k_pool, v_pool, k_resp, v_resp,
+                       part_o, part_m, part_l, workspace=None, stream=None) -> None:
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ls_replay_attn_fwd(
+        ctypes.byref(shape), ctypes.byref(pt), _ptr(q, bf, "q"), _ptr(k_pool, bf, "k_pool"),
+        _ptr(v_pool, bf, "v_pool"), _ptr(k_resp, bf, "k_resp"), _ptr(v_resp, bf, "v_resp"),
+        _ptr(part_o, f32, "part_o"), _ptr(part_m, f32, "part_m"), _ptr(part_l, f32, "part_l"),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _check("ls_replay_attn_fwd", st)
+
+
+def ls_lse_merge(num_parts: int, rows: int, head_dim: int, part_o, part_m, part_l, o_bf16, lse,
+                 stream=None) -> None:
+    f32 = torch.float32
+    st = lib().ls_lse_merge(num_parts, rows, head_dim, _ptr(part_o, f32, "part_o"),
+                            _ptr(part_m, f32, "part_m"), _ptr(part_l, f32, "part_l"),
+                            _ptr(o_bf16, torch.bfloat16, "o"), _ptr(lse, f32, "lse"),
+                            _stream(stream))
+    _check("ls_lse_merge", st)
+
+
+def ls_replay_attn_bwd(shape: AttnShape, pt: PageTable, q, k_pool, v_pool, k_resp, v_resp, o, lse,
+                       d_o, dq, dk_resp, dv_resp, workspace, stream=None) -> None:
+    bf, f32 = torch.bfloat16, torch.float32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ls_replay_attn_bwd(
+        ctypes.byref(shape), ctypes.byref(pt), _ptr(q, bf, "q"), _ptr(k_pool, bf, "k_pool"),
+        _ptr(v_pool, bf, "v_pool"), _ptr(k_resp, bf, "k_resp"), _ptr(v_resp, bf, "v_resp"),
+        _ptr(o, bf, "o"), _ptr(lse, f32, "lse"), _ptr(d_o, bf, "d_o"), _ptr(dq, f32, "dq"),
+        _ptr(dk_resp, f32, "dk_resp"), _ptr(dv_resp, f32, "dv_resp"), _ptr(workspace), ws_bytes,
+        _stream(stream))
+    _check("ls_replay_attn_bwd", st)
+
+
+def ls_timing_enable(on: bool) -> None:
+    _check("ls_timing_enable", lib().ls_timing_enable(1 if on else 0))
+
+
+def ls_timing_reset() -> None:
+    _check("ls_timing_reset", lib().ls_timing_reset())
+
+
+def ls_timing_read(kernel: str) -> Tuple[int, float]:
+    n = ctypes.c_int32(0)
+    ms = ctypes.c_double(0.0)
+    _check("ls_timing_read", lib().ls_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

@@ -1,0 +1,285 @@
+// Response-only backward of replay attention.
+//
+// The prompt state is stopgrad (DeepRead summary page, "Method"): no gradient
+// is formed for the prompt K/V.  What remains (LongStraw review page,
+// section 2 and the section 7 mind map):
+//   * dQ over the prompt keys of each split, recomputing P = exp(x - LSE) from
+//     the saved LSE -- one partial per split, later summed in split order (the
+//     one-GPU stand-in for the pages' dQ all-reduce across CP ranks);
+//   * dQ over the causal response block (one more partial);
+//   * dK, dV of the response keys (KV-stationary, summed over the query heads
+//     of each KV group inside one workgroup, so no atomics are needed).
+//
+// dQ kernel mapping (4 waves x 32 query rows): per key block
+//   S^T  = K Q^T      (A = K rows from LDS, B = Q in registers)
+//   dP^T = V dO^T     (A = V rows from LDS, B = dO in registers)
+//   dS^T = P^T (dP^T - D)                    with P^T = exp2(S^T*s*log2e - LSE*log2e)
+//   dQ^T += K^T dS^T  (A = K^T gathered from the same K tile, B = dS^T in registers)
+// so dQ^T keeps one query per lane, like O^T in the forward.
+#include "ls_device.hpp"
+
+namespace ls {
+
+template <int D, bool RESP>
+__global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
+  constexpr int NKK = D / 16;
+  constexpr int NMT = D / 32;
+  constexpr int TILE = kBN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // [buf][K,V]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, lq = lane & 31;
+
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_unit = a.mtiles * a.hkv;
+  const int unit = w / per_unit;
+  const int rem = w - unit * per_unit;
+  const int kv = rem / a.mtiles;
+  const int mtile = rem - kv * a.mtiles;
+  const int GR = (a.hq / a.hkv) * a.R;
+  const int m0 = mtile * kBwdRows;
+  const int m = m0 + 32 * wave + lq;
+  const bool rvalid = m < GR;
+  const size_t row0 = (size_t)kv * GR;
+  const size_t row = row0 + min(m, GR - 1);
+  const int qi = m % a.R;
+
+  const KeyWalk<D, RESP> walk(a, kv, unit, m0, kBwdRows);
+  const int nblocks = walk.nblocks;
+  const int slot = a.slot_base + unit;
+
+  // Q and dO as B operands (column = query m, k = 16*kk + 8*hf + e)
+  bf16x8 qr[NKK], dor[NKK];
+  {
+    const uint16_t* qp = a.q + row * D + 8 * hf;
+    const uint16_t* dp = a.d_o + row * D + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qr[kk] = ld_bf16x8(qp + 16 * kk);
+      dor[kk] = ld_bf16x8(dp + 16 * kk);
+    }
+  }
+  // invalid rows: P = exp2(x - inf) = 0, so they contribute nothing
+  const float lse2 = rvalid ? a.lse[row] * kLog2e : kInf;
+  const float dval = rvalid ? a.dvals[row] : 0.f;
+
+  f32x16 acc[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+
+  const Lanes32<D> tl(hf, lq);
+  auto issue = [&](int b, int buf, int& nvalid, int& key0) {
+    walk.issue(b, smem + buf * 2 * TILE, smem + buf * 2 * TILE + TILE, wave, lane, nvalid, key0);
+  };
+  int cur_nv = 0, cur_k0 = 0;
+  if (nblocks > 0) issue(0, 0, cur_nv, cur_k0);
+  wait_async_loads();
+  __syncthreads();
+
+  auto step = [&](int b, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    int nx_nv = 0, nx_k0 = 0;
+    // the other buffer was last read in block b-1, before the barrier that ended it
+    if (b + 1 < nblocks) issue(b + 1, BUF ^ 1, nx_nv, nx_k0);
+
+    if (cur_nv > 0) {
+      const uint16_t* kl = smem + BUF * 2 * TILE;
+      const uint16_t* vl = kl + TILE;
+
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s = mfma32(tl.row8(kl, kk), qr[kk], s);
+        dp = mfma32(tl.row8(vl, kk), dor[kk], dp);
+      }
+
+      // dS^T = P^T (dP^T - D), rounded to bf16 as the B operand of dQ^T
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = crow(r, hf);
+        bool ok = key < cur_nv;
+        if (RESP) ok = ok && (cur_k0 + key <= qi);
+        const float p = ok ? __builtin_amdgcn_exp2f(s[r] * a.s2 - lse2) : 0.f;
+        dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - dval));
+      }
+
+      // dQ^T[d][query] += sum_key K[key][d] dS^T[key][query]
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma32(tl.col8(kl, ks, mt), dsb[ks], acc[mt]);
+      }
+    }
+
+    cur_nv = nx_nv;
+    cur_k0 = nx_k0;
+    wait_async_loads();
+    __syncthreads();
+  };
+
+  for (int b = 0; b < nblocks; b += 2) {
+    step(b, IntC<0>{});
+    if (b + 1 < nblocks) step(b + 1, IntC<1>{});
+  }
+
+  if (rvalid) {
+    const size_t rows_total = (size_t)a.hq * a.R;
+    float* op = a.dq_slots + ((size_t)slot * rows_total + row0 + m) * D + 4 * hf;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 v;
+        v.x = acc[mt][4 * r4 + 0] * a.scale;
+        v.y = acc[mt][4 * r4 + 1] * a.scale;
+        v.z = acc[mt][4 * r4 + 2] * a.scale;
+        v.w = acc[mt][4 * r4 + 3] * a.scale;
+        *reinterpret_cast<float4*>(op + 32 * mt + 8 * r4) = v;
+      }
+    }
+  }
+}
+
+// dK or dV of 32 response keys [j0, j0+32) of KV head kv, one wave per
+// workgroup, key-stationary: loops over every query head of the group and every
+// query block i0 >= j0, accumulating
+//   DV:  dV^T[d][key] += sum_query dO[query][d] P[query][key]
+//   DK:  dK^T[d][key] += sum_query Q[query][d]  dS[query][key]
+// with S = Q K^T and dP = dO V^T recomputed in the (query x key) orientation.
+// dV and dK are separate launches so each needs only one 128-register
+// accumulator set.
+template <int D, bool DK>
+__global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
+  constexpr int NKK = D / 16;
+  constexpr int NMT = D / 32;
+  constexpr int TILE = kBN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // K_r, V_r, Q, dO
+  __shared__ float s_lse2[kBN], s_dval[kBN];
+
+  const int lane = threadIdx.x, hf = lane >> 5, lq = lane & 31;
+  const int kv = blockIdx.y;
+  const int j0 = blockIdx.x * kBN;
+  const int g = a.hq / a.hkv;
+  uint16_t* kt = smem;
+  uint16_t* vt = smem + TILE;
+  uint16_t* qt = smem + 2 * TILE;
+  uint16_t* dt = smem + 3 * TILE;
+
+  const int nkeys = min(kBN, a.R - j0);
+  {
+    const size_t off = ((size_t)kv * a.R + j0) * D;
+    tile_load_async<D, 1>(kt, a.k + off, nkeys, 0, lane);
+    if (DK) tile_load_async<D, 1>(vt, a.v + off, nkeys, 0, lane);
+  }
+  const Lanes32<D> tl(hf, lq);
+  const int key = j0 + lq;  // this lane's key column
+
+  f32x16 acc[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+
+  for (int hh = 0; hh < g; ++hh) {
+    const int h = kv * g + hh;
+    for (int i0 = j0; i0 < a.R; i0 += kBN) {
+      const int nq = min(kBN, a.R - i0);
+      const size_t qoff = ((size_t)h * a.R + i0) * D;
+      __syncthreads();  // previous block's reads of qt/dt and s_* are done
+      tile_load_async<D, 1>(qt, a.q + qoff, nq, 0, lane);
+      tile_load_async<D, 1>(dt, a.d_o + qoff, nq, 0, lane);
+      if (lane < kBN) {
+        const bool ok = lane < nq;
+        const size_t r = (size_t)h * a.R + i0 + (ok ? lane : 0);
+        s_lse2[lane] = ok ? a.lse[r] * kLog2e : kInf;
+        s_dval[lane] = ok ? a.dvals[r] : 0.f;
+      }
+      wait_async_loads();
+      __syncthreads();
+
+      // S[query][key] = sum_d Q[query][d] K[key][d]; dP likewise with dO, V
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s = mfma32(tl.row8(qt, kk), tl.row8(kt, kk), s);
+        if (DK) dp = mfma32(tl.row8(dt, kk), tl.row8(vt, kk), dp);
+      }
+
+      // P (or dS) as the B operand: register 8*ks + e holds query kperm(ks,hf,e)
+      bf16x8 pb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = crow(r, hf);
+        const bool ok = (q < nq) && (key < a.R) && (key <= i0 + q);
+        const float p = ok ? __builtin_amdgcn_exp2f(s[r] * a.s2 - s_lse2[q]) : 0.f;
+        const float val = DK ? p * (dp[r] - s_dval[q]) : p;
+        pb[r >> 3][r & 7] = to_bf16(val);
+      }
+
+      // dV^T (or dK^T)[d][key] += sum_query X^T[d][query] pb[query][key]
+      const uint16_t* xt = DK ? qt : dt;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma32(tl.col8(xt, ks, mt), pb[ks], acc[mt]);
+      }
+    }
+  }
+
+  if (key < a.R) {
+    const float mul = DK ? a.scale : 1.f;
+    float* op = (DK ? a.dk : a.dv) + ((size_t)kv * a.R + key) * D + 4 * hf;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 v;
+        v.x = acc[mt][4 * r4 + 0] * mul;
+        v.y = acc[mt][4 * r4 + 1] * mul;
+        v.z = acc[mt][4 * r4 + 2] * mul;
+        v.w = acc[mt][4 * r4 + 3] * mul;
+        *reinterpret_cast<float4*>(op + 32 * mt + 8 * r4) = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  dim3 g(grid), b(256);
+  if (head_dim == 256) {
+    if (resp) hipLaunchKernelGGL((k_bwd_dq<256, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_bwd_dq<256, false>), g, b, 0, s, a);
+  } else {
+    if (resp) hipLaunchKernelGGL((k_bwd_dq<128, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_bwd_dq<128, false>), g, b, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s) {
+  dim3 g((a.R + kBN - 1) / kBN, a.hkv), b(64);
+  if (head_dim == 256) {
+    hipLaunchKernelGGL((k_bwd_resp_kv<256, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((k_bwd_resp_kv<256, true>), g, b, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_bwd_resp_kv<128, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((k_bwd_resp_kv<128, true>), g, b, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ls

@@ -1,0 +1,62 @@
+// Internal declarations shared by the host API (ls_api.cpp) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace ls {
+
+constexpr int kPage = 256;       // prompt tokens per page (only size supported)
+constexpr int kBN = 32;          // keys per inner block (one 32-row MFMA tile)
+constexpr int kFwdRows = 128;    // query rows per forward workgroup (4 waves x 32)
+constexpr int kBwdRows = 128;    // query rows per dQ workgroup (4 waves x 32)
+constexpr int kTargetWGs = 256;  // one workgroup per CU on MI355X (256 CUs)
+constexpr int kMaxChunks = 64;   // cap on internal sub-splits per split
+
+// Source of keys for one launch: the paged prompt pool (via the page table) or
+// the contiguous response K/V (causal).
+struct AttnArgs {
+  const uint16_t* q;      // bf16 [Hq, R, d]
+  const uint16_t* k;      // bf16 pool [phys, Hkv, 256, d]  or response [Hkv, R, d]
+  const uint16_t* v;
+  const int32_t* l2p;     // device page map (paged only)
+  const int32_t* order;   // device split-major page list (paged only)
+  const int32_t* offs;    // device split offsets (paged only)
+  int64_t prompt_len;
+  int32_t num_pages, num_phys, chunks, chunk_pages;
+  int32_t hq, hkv, R, mtiles;
+  float s2;               // scale * log2(e)
+  float scale;
+  // forward outputs (slot arrays): o [slots, Hq*R, d], m/l [slots, Hq*R]
+  float* o;
+  float* m;
+  float* l;
+  int32_t slot_base;
+  // backward inputs/outputs
+  const uint16_t* d_o;    // bf16 [Hq, R, d]
+  const float* lse;       // fp32 [Hq, R]
+  const float* dvals;     // fp32 [Hq, R]  D = <dO, O>
+  float* dq_slots;        // fp32 [slots, Hq*R, d]
+  float* dk;              // fp32 [Hkv, R, d]
+  float* dv;
+};
+
+hipError_t launch_fwd(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s);
+hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s);
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s);
+
+// Merge `nper` consecutive parts per group: group c reads parts
+// [c*nper, (c+1)*nper).  final=true writes bf16 O and natural-log LSE;
+// final=false writes a combined fp32 partial (o, m, l) per group.
+hipError_t launch_merge(int groups, int nper, int64_t rows, int head_dim, const float* po,
+                        const float* pm, const float* pl, bool final, void* out_o,
+                        float* out_m, float* out_l, hipStream_t s);
+hipError_t launch_bwd_dot(int64_t rows, int head_dim, const uint16_t* d_o, const uint16_t* o,
+                          float* dvals, hipStream_t s);
+hipError_t launch_dq_reduce(int nslots, int64_t elems, const float* slots, float* dq,
+                            hipStream_t s);
+
+}  // namespace ls

@@ -1,0 +1,147 @@
+// Small HBM-bound kernels of the replay path:
+//   * the exact log-sum-exp merge of partial attention (the pages' global
+//     LSE/output composition across CP ranks; LongStraw review page, section 7
+//     mind map, "Qwen3.6-27B implementation"), also used to fold internal
+//     sub-splits of one split back into that split's partial;
+//   * D = rowsum(dO * O) for the backward;
+//   * the ordered sum of the per-split dQ partials (the one-GPU stand-in for
+//     the pages' dQ all-reduce; review page, section 2).
+// All are streaming kernels: one pass over their inputs with 16-byte accesses.
+#include "ls_device.hpp"
+
+namespace ls {
+
+// One row per D/4 threads; thread e4 owns elements [4*e4, 4*e4 + 4).
+template <int D, bool FINAL>
+__global__ void __launch_bounds__(256) k_merge(int nper, int64_t rows, const float* __restrict__ po,
+                                               const float* __restrict__ pm,
+                                               const float* __restrict__ pl, void* out_o,
+                                               float* out_m, float* out_l) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int grp = blockIdx.y;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int e4 = threadIdx.x % TPR;
+  if (row >= rows) return;
+  const int c0 = grp * nper;
+
+  float big = -kInf;
+  for (int c = 0; c < nper; ++c) {
+    const size_t i = (size_t)(c0 + c) * rows + row;
+    if (pl[i] > 0.f) big = fmaxf(big, pm[i]);
+  }
+  float tot = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (big != -kInf) {
+    for (int c = 0; c < nper; ++c) {
+      const size_t i = (size_t)(c0 + c) * rows + row;
+      const float l = pl[i];
+      if (!(l > 0.f)) continue;
+      const float w = l * expf(pm[i] - big);
+      tot += w;
+      const float4 o = *reinterpret_cast<const float4*>(po + i * D + 4 * e4);
+      acc.x += w * o.x;
+      acc.y += w * o.y;
+      acc.z += w * o.z;
+      acc.w += w * o.w;
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  acc.x *= inv;
+  acc.y *= inv;
+  acc.z *= inv;
+  acc.w *= inv;
+  if (FINAL) {
+    __bf16* o = reinterpret_cast<__bf16*>(out_o) + row * D + 4 * e4;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v = {to_bf16(acc.x), to_bf16(acc.y), to_bf16(acc.z), to_bf16(acc.w)};
+    *reinterpret_cast<bf16x4*>(o) = v;
+    if (e4 == 0) out_m[row] = tot > 0.f ? big + logf(tot) : -kInf;  // LSE
+  } else {
+    const size_t i = (size_t)grp * rows + row;
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out_o) + i * D + 4 * e4) = acc;
+    if (e4 == 0) {
+      out_m[i] = tot > 0.f ? big : -kInf;
+      out_l[i] = tot;
+    }
+  }
+}
+
+// D[row] = sum_d dO[row][d] * O[row][d]; D/8 lanes per row, 8 elements each.
+template <int D>
+__global__ void __launch_bounds__(256) k_bwd_dot(int64_t rows, const uint16_t* __restrict__ d_o,
+                                                 const uint16_t* __restrict__ o,
+                                                 float* __restrict__ dvals) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int e8 = threadIdx.x % TPR;
+  float sum = 0.f;
+  if (row < rows) {
+    const u16x8 a = *reinterpret_cast<const u16x8*>(d_o + row * D + 8 * e8);
+    const u16x8 b = *reinterpret_cast<const u16x8*>(o + row * D + 8 * e8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      sum += __uint_as_float((uint32_t)a[e] << 16) * __uint_as_float((uint32_t)b[e] << 16);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (row < rows && e8 == 0) dvals[row] = sum;
+}
+
+// dq[e] = sum_{s < nslots} slots[s][e], in slot order (deterministic).
+__global__ void __launch_bounds__(256) k_dq_reduce(int nslots, int64_t n4,
+                                                   const float4* __restrict__ slots,
+                                                   float4* __restrict__ dq) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float4 acc = slots[i];
+    for (int s = 1; s < nslots; ++s) {
+      const float4 v = slots[(size_t)s * n4 + i];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    dq[i] = acc;
+  }
+}
+
+hipError_t launch_merge(int groups, int nper, int64_t rows, int head_dim, const float* po,
+                        const float* pm, const float* pl, bool final, void* out_o, float* out_m,
+                        float* out_l, hipStream_t s) {
+  if (rows <= 0 || groups <= 0) return hipSuccess;
+  const int rpb = 256 / (head_dim / 4);
+  dim3 g((unsigned)((rows + rpb - 1) / rpb), groups), b(256);
+  if (head_dim == 256) {
+    if (final) hipLaunchKernelGGL((k_merge<256, true>), g, b, 0, s, nper, rows, po, pm, pl, out_o, out_m, out_l);
+    else hipLaunchKernelGGL((k_merge<256, false>), g, b, 0, s, nper, rows, po, pm, pl, out_o, out_m, out_l);
+  } else {
+    if (final) hipLaunchKernelGGL((k_merge<128, true>), g, b, 0, s, nper, rows, po, pm, pl, out_o, out_m, out_l);
+    else hipLaunchKernelGGL((k_merge<128, false>), g, b, 0, s, nper, rows, po, pm, pl, out_o, out_m, out_l);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dot(int64_t rows, int head_dim, const uint16_t* d_o, const uint16_t* o,
+                          float* dvals, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int rpb = 256 / (head_dim / 8);
+  dim3 g((unsigned)((rows + rpb - 1) / rpb)), b(256);
+  if (head_dim == 256) hipLaunchKernelGGL((k_bwd_dot<256>), g, b, 0, s, rows, d_o, o, dvals);
+  else hipLaunchKernelGGL((k_bwd_dot<128>), g, b, 0, s, rows, d_o, o, dvals);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_reduce(int nslots, int64_t elems, const float* slots, float* dq,
+                            hipStream_t s) {
+  const int64_t n4 = elems / 4;
+  if (n4 <= 0) return hipSuccess;
+  const int64_t want = (n4 + 255) / 256;
+  dim3 g((unsigned)(want < 4096 ? want : 4096)), b(256);
+  hipLaunchKernelGGL(k_dq_reduce, g, b, 0, s, nslots, n4, reinterpret_cast<const float4*>(slots),
+                     reinterpret_cast<float4*>(dq));
+  return hipGetLastError();
+}
+
+}  // namespace ls

@@ -1,0 +1,143 @@
+"""Replay driver: the prompt's paged K/V with its device page table, and the
+calls that replay one response (forward, LSE merge, response-only backward)
+or a whole group of responses one after another.
+
+The group loop follows the pages' serial suffix replay: the shared prompt is
+captured once and each response branch is replayed, back-propagated and freed
+before the next one, so peak memory follows the longest response rather than
+the group size (DeepRead summary page, "Method"; LongStraw review page,
+section 2, item 3).  Everything here is allocation and argument marshalling;
+the arithmetic runs in libls_replay.so.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Iterable, List, Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+class PromptCache:
+    """A detached prompt: bf16 K/V pools ``[num_phys, Hkv, 256, d]`` (never
+    written by this package) and the page table that maps its logical pages to
+    pool slots and deals them to ``num_splits`` emulated context-parallel
+    ranks."""
+
+    def __init__(self, k_pool: torch.Tensor, v_pool: torch.Tensor, prompt_len: int,
+                 l2p=None, num_splits: int = 1, policy: int = B.LS_SPLIT_CONTIGUOUS,
+                 block_pages: int = 1, owner=None):
+        if k_pool.shape != v_pool.shape or k_pool.dim() != 4:
+            raise ValueError("k_pool and v_pool must both be [num_phys, Hkv, 256, d]")
+        self.k_pool, self.v_pool = k_pool, v_pool
+        self.prompt_len = int(prompt_len)
+        self.num_phys = int(k_pool.shape[0])
+        self.hkv = int(k_pool.shape[1])
+        self.head_dim = int(k_pool.shape[3])
+        self.num_pages = (self.prompt_len + B.PAGE_SIZE - 1) // B.PAGE_SIZE
+        self.num_splits = int(num_splits)
+        l2p_np = (np.arange(self.num_pages, dtype=np.int32) if l2p is None
+                  else np.asarray(l2p.cpu() if isinstance(l2p, torch.Tensor) else l2p, dtype=np.int32))
+        order, offs = B.ls_kv_page_table(self.num_pages, B.PAGE_SIZE, self.prompt_len, l2p_np,
+                                         self.num_phys, self.num_splits, policy, block_pages, owner)
+        dev = k_pool.device
+        self.order = order
+        self.split_offsets_host = np.ascontiguousarray(offs)  # kept alive: the table points at it
+        self._l2p_dev = torch.from_numpy(np.ascontiguousarray(l2p_np)).to(dev)
+        self._order_dev = torch.from_numpy(np.ascontiguousarray(order)).to(dev)
+        self._offs_dev = torch.from_numpy(self.split_offsets_host.copy()).to(dev)
+        self.pt = B.PageTable(
+            self._l2p_dev.data_ptr() if self.num_pages else 0,
+            self._order_dev.data_ptr() if self.num_pages else 0,
+            self._offs_dev.data_ptr(), self.split_offsets_host.ctypes.data,
+            self.num_pages, self.num_splits, self.num_phys)
+
+    def shape(self, q: torch.Tensor, scale: Optional[float] = None) -> B.AttnShape:
+        hq, r, d = q.shape
+        if d != self.head_dim:
+            raise ValueError("head_dim mismatch between q and the pools")
+        s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        return B.make_shape(hq, self.hkv, d, self.prompt_len, r, s)
+
+
+@dataclass
+class ForwardResult:
+    o: torch.Tensor        # bf16 [Hq, R, d]
+    lse: torch.Tensor      # fp32 [Hq, R]
+    part_o: torch.Tensor   # fp32 [S+1, Hq, R, d]
+    part_m: torch.Tensor   # fp32 [S+1, Hq, R]
+    part_l: torch.Tensor
+
+
+def replay_forward(cache: PromptCache, q, k_resp, v_resp, scale=None, stream=None) -> ForwardResult:
+    """Partial attention per split + the causal response block, then the exact
+    LSE merge."""
+    sh = cache.shape(q, scale)
+    hq, r, d = q.shape
+    dev = q.device
+    nparts = cache.num_splits + 1
+    part_o = torch.empty(nparts, hq, r, d, dtype=torch.float32, device=dev)
+    part_m = torch.empty(nparts, hq, r, dtype=torch.float32, device=dev)
+    part_l = torch.empty(nparts, hq, r, dtype=torch.float32, device=dev)
+    wsb = B.ls_replay_attn_fwd_workspace(sh, cache.pt)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+    B.ls_replay_attn_fwd(sh, cache.pt, q, cache.k_pool, cache.v_pool, k_resp, v_resp,
+                         part_o, part_m, part_l, ws, stream)
+    o = torch.empty(hq, r, d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(hq, r, dtype=torch.float32, device=dev)
+    B.ls_lse_merge(nparts, hq * r, d, part_o, part_m, part_l, o, lse, stream)
+    del ws
+    return ForwardResult(o, lse, part_o, part_m, part_l)
+
+
+def replay_backward(cache: PromptCache, q, k_resp, v_resp, o, lse, d_o, scale=None, stream=None):
+    """Response-only backward: returns ``(dq, dk_resp, dv_resp)`` in fp32.
+    The prompt pools get no gradient."""
+    sh = cache.shape(q, scale)
+    hq, r, d = q.shape
+    dev = q.device
+    dq = torch.empty(hq, r, d, dtype=torch.float32, device=dev)
+    dk = torch.empty(cache.hkv, r, d, dtype=torch.float32, device=dev)
+    dv = torch.empty(cache.hkv, r, d, dtype=torch.float32, device=dev)
+    wsb = B.ls_replay_attn_bwd_workspace(sh, cache.pt)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    B.ls_replay_attn_bwd(sh, cache.pt, q, cache.k_pool, cache.v_pool, k_resp, v_resp, o, lse, d_o,
+                         dq, dk, dv, ws, stream)
+    del ws
+    return dq, dk, dv
+
+
+@dataclass
+class Member:
+    """One response branch of a group: its queries, its own K/V and the
+    upstream gradient of its attention output."""
+    q: torch.Tensor
+    k_resp: torch.Tensor
+    v_resp: torch.Tensor
+    d_o: torch.Tensor
+
+
+def replay_member(cache: PromptCache, m: Member, scale=None, stream=None):
+    """Forward, merge and backward of one member.  Returns
+    ``(ForwardResult, dq, dk_resp, dv_resp)``."""
+    fwd = replay_forward(cache, m.q, m.k_resp, m.v_resp, scale, stream)
+    dq, dk, dv = replay_backward(cache, m.q, m.k_resp, m.v_resp, fwd.o, fwd.lse, m.d_o, scale, stream)
+    return fwd, dq, dk, dv
+
+
+def replay_group(cache: PromptCache, members: Iterable[Member], consume=None, scale=None,
+                 stream=None) -> List:
+    """Serial replay of a group against one shared prompt.  Each member's
+    partials, outputs and gradients are handed to ``consume(index, fwd, dq,
+    dk, dv)`` (if given) and then released before the next member starts, so
+    at most one member's buffers are alive at a time.  Returns whatever
+    ``consume`` returned, per member."""
+    out = []
+    for i, m in enumerate(members):
+        fwd, dq, dk, dv = replay_member(cache, m, scale, stream)
+        out.append(consume(i, fwd, dq, dk, dv) if consume is not None else None)
+        del fwd, dq, dk, dv
+    return out

@@ -1,0 +1,244 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/ls_replay.h declares;
+* ls_kv_page_table equals the oracle's page split, bit for bit;
+* every argument check returns its status before any HIP call (so these run
+  on a machine without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import response_replay_attention_amd as rra
+from response_replay_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ls_replay.h")
+
+LS_OK, INVALID, UNSUPPORTED, PAGE_RANGE, WORKSPACE = 0, -1, -2, -3, -4
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(ls_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rra.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 11, declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(B.EXPORTS) == declared
+
+
+def test_version_and_status_strings():
+    assert rra.ls_version() >= 100
+    for s in (0, -1, -2, -3, -4, -5):
+        assert rra.ls_status_string(s)
+    assert rra.ls_status_string(7) == "unknown status"
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_page_table_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    num_pages = int(rng.integers(0, 70))
+    num_splits = int(rng.integers(1, 12))
+    policy = int(rng.integers(0, 3))
+    block = int(rng.integers(1, 5))
+    owner = rng.integers(0, num_splits, num_pages).astype(np.int32)
+    phys = num_pages + int(rng.integers(0, 5))
+    l2p = rng.permutation(phys)[:num_pages].astype(np.int32)
+    prompt_len = num_pages * 256 - (int(rng.integers(0, 256)) if num_pages else 0)
+    order, offs = rra.ls_kv_page_table(num_pages, 256, prompt_len, l2p, phys, num_splits, policy,
+                                       block, owner)
+    eo, eoff = oracle.split_pages(num_pages, num_splits, policy, block, owner)
+    assert list(order) == eo
+    assert list(offs) == eoff
+
+
+def test_page_table_oracle_properties():
+    """Pins of the page-split oracle (definitions of the three policies)."""
+    for n, s in ((0, 3), (1, 1), (10, 3), (8192, 8), (17408, 16), (97, 8)):
+        for policy, block in ((0, 1), (1, 1), (1, 4)):
+            order, offs = oracle.split_pages(n, s, policy, block)
+            assert sorted(order) == list(range(n))
+            assert offs[0] == 0 and offs[-1] == n and all(a <= b for a, b in zip(offs, offs[1:]))
+            for c in range(s):
+                pages = order[offs[c]:offs[c + 1]]
+                assert pages == sorted(pages)
+                if policy == 0:
+                    assert pages == list(range(pages[0], pages[0] + len(pages))) if pages else True
+                    sizes = [offs[i + 1] - offs[i] for i in range(s)]
+                    assert max(sizes) - min(sizes) <= 1 and sizes == sorted(sizes, reverse=True)
+                else:
+                    assert all((p // block) % s == c for p in pages)
+    # the 2M prefix over 8 splits: 1024 consecutive pages each
+    order, offs = oracle.split_pages(8192, 8, 0)
+    assert offs == [1024 * c for c in range(9)]
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(num_pages=-1), INVALID),
+    (dict(num_splits=0), INVALID),
+    (dict(page_size=128), UNSUPPORTED),
+    (dict(prompt_len=5 * 256 + 1), INVALID),        # would need 6 pages
+    (dict(policy=9), INVALID),
+    (dict(policy=1, block_pages=0), INVALID),
+    (dict(policy=2, owner=[0, 1, 2, 3, 4]), INVALID),  # owner out of range (3 splits)
+    (dict(l2p=[0, 1, 2, 3, 9]), PAGE_RANGE),          # slot past the pool
+    (dict(l2p=[0, 1, 2, 2, 3]), PAGE_RANGE),          # a slot used twice
+    (dict(l2p=[0, 1, -1, 2, 3]), PAGE_RANGE),
+    (dict(l2p=None, num_phys_pages=4), PAGE_RANGE),
+])
+def test_page_table_rejects(args, status):
+    base = dict(num_pages=5, page_size=256, prompt_len=5 * 256, l2p=[4, 3, 2, 1, 0],
+                num_phys_pages=6, num_splits=3, policy=0, block_pages=1, owner=None)
+    base.update(args)
+    with pytest.raises(B.LsError) as e:
+        rra.ls_kv_page_table(**base)
+    assert e.value.status == status
+
+
+def test_page_table_partial_last_page_and_empty_prompt():
+    order, offs = rra.ls_kv_page_table(3, 256, 2 * 256 + 1, [2, 0, 1], 3, 2, 0)
+    assert list(order) == [0, 1, 2] and list(offs) == [0, 2, 3]
+    order, offs = rra.ls_kv_page_table(0, 256, 0, None, 0, 4, 0)
+    assert len(order) == 0 and list(offs) == [0, 0, 0, 0, 0]
+
+
+# ------------------------------------------------ validation of the GPU calls
+FAKE = 0x10000  # an aligned, never dereferenced "device" address
+
+
+def _shape(**kw):
+    d = dict(num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=256, prompt_len=4 * 256,
+             resp_len=64, scale=1 / 16)
+    d.update(kw)
+    return B.AttnShape(**d)
+
+
+_offs_keep = []
+
+
+def _table(num_pages=4, num_splits=2, offs=None, **kw):
+    o = np.array(offs if offs is not None else [0, 2, 4][: num_splits + 1], dtype=np.int32)
+    _offs_keep.append(o)
+    d = dict(l2p=FAKE, order=FAKE, split_offsets=FAKE, split_offsets_host=o.ctypes.data,
+             num_pages=num_pages, num_splits=num_splits, num_phys_pages=num_pages)
+    d.update(kw)
+    return B.PageTable(**d)
+
+
+def _fwd(sh, pt, **ptrs):
+    p = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, k_resp=FAKE, v_resp=FAKE, part_o=FAKE,
+             part_m=FAKE, part_l=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    p.update(ptrs)
+    return rra.lib().ls_replay_attn_fwd(ctypes.byref(sh), ctypes.byref(pt), p["q"], p["k_pool"],
+                                        p["v_pool"], p["k_resp"], p["v_resp"], p["part_o"],
+                                        p["part_m"], p["part_l"], p["ws"], p["ws_bytes"], None)
+
+
+def _bwd(sh, pt, **ptrs):
+    p = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, k_resp=FAKE, v_resp=FAKE, o=FAKE, lse=FAKE,
+             d_o=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    p.update(ptrs)
+    return rra.lib().ls_replay_attn_bwd(ctypes.byref(sh), ctypes.byref(pt), p["q"], p["k_pool"],
+                                        p["v_pool"], p["k_resp"], p["v_resp"], p["o"], p["lse"],
+                                        p["d_o"], p["dq"], p["dk"], p["dv"], p["ws"],
+                                        p["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("shape_kw,status", [
+    (dict(head_dim=64), UNSUPPORTED),
+    (dict(page_size=128), UNSUPPORTED),
+    (dict(num_q_heads=25), INVALID),       # Hq % Hkv != 0
+    (dict(resp_len=0), INVALID),
+    (dict(prompt_len=-1), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(prompt_len=5 * 256), INVALID),   # table has 4 pages, prompt needs 5
+    (dict(resp_len=1 << 20), UNSUPPORTED), # Hq*R*d >= 2^31
+])
+def test_fwd_bwd_reject_bad_shapes(shape_kw, status):
+    sh, pt = _shape(**shape_kw), _table()
+    assert _fwd(sh, pt) == status
+    assert _bwd(sh, pt) == status
+    assert rra.ls_replay_attn_fwd_workspace(sh, pt) == 0
+
+
+@pytest.mark.parametrize("table_kw", [
+    dict(offs=[0, 3, 2]),                   # decreasing offsets
+    dict(offs=[1, 2, 4]),                   # not starting at 0
+    dict(offs=[0, 2, 3]),                   # not ending at num_pages
+    dict(num_splits=0),
+    dict(num_phys_pages=3),                 # fewer slots than pages
+    dict(l2p=0),
+    dict(order=0),
+    dict(split_offsets=0),
+    dict(split_offsets_host=0),
+])
+def test_fwd_bwd_reject_bad_tables(table_kw):
+    sh, pt = _shape(), _table(**table_kw)
+    assert _fwd(sh, pt) == INVALID
+    assert _bwd(sh, pt) == INVALID
+
+
+@pytest.mark.parametrize("name", ["q", "k_resp", "v_resp", "part_o", "part_m", "part_l", "k_pool"])
+def test_fwd_rejects_null_or_misaligned(name):
+    sh, pt = _shape(), _table()
+    assert _fwd(sh, pt, **{name: 0}) == INVALID
+    assert _fwd(sh, pt, **{name: FAKE + 2}) == INVALID
+
+
+@pytest.mark.parametrize("name", ["q", "o", "lse", "d_o", "dq", "dk", "dv", "v_pool"])
+def test_bwd_rejects_null_or_misaligned(name):
+    sh, pt = _shape(), _table()
+    assert _bwd(sh, pt, **{name: 0}) == INVALID
+    assert _bwd(sh, pt, **{name: FAKE + 4}) == INVALID
+
+
+def test_workspace_checks():
+    sh, pt = _shape(), _table()
+    need = rra.ls_replay_attn_bwd_workspace(sh, pt)
+    assert need >= 24 * 64 * 4 + 3 * 24 * 64 * 256 * 4   # D + (2 splits + response) dQ slots
+    assert _bwd(sh, pt, ws_bytes=need - 1) == WORKSPACE
+    assert _bwd(sh, pt, ws=0) == WORKSPACE
+    # a short prompt with 2 splits needs internal chunks -> forward workspace
+    big = _shape(prompt_len=262_144, resp_len=1024)
+    bt = _table(num_pages=1024, num_splits=1, offs=[0, 1024])
+    need = rra.ls_replay_attn_fwd_workspace(big, bt)
+    assert need > 0
+    assert _fwd(big, bt, ws_bytes=need - 1) == WORKSPACE
+    assert _fwd(big, bt, ws=0) == WORKSPACE
+
+
+def test_prompt_free_table_needs_no_pools():
+    """P = 0: no pages, pools may be NULL; validation passes up to the launch."""
+    sh = _shape(prompt_len=0)
+    pt = _table(num_pages=0, num_splits=2, offs=[0, 0, 0], l2p=0, order=0)
+    assert rra.ls_replay_attn_fwd_workspace(sh, pt) == 0
+    assert rra.ls_replay_attn_bwd_workspace(sh, pt) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_parts=0), INVALID), (dict(rows=0), INVALID), (dict(head_dim=96), UNSUPPORTED),
+    (dict(o=0), INVALID), (dict(lse=FAKE + 8), INVALID), (dict(pm=0), INVALID),
+])
+def test_merge_rejects(kw, status):
+    p = dict(num_parts=9, rows=100, head_dim=256, po=FAKE, pm=FAKE, pl=FAKE, o=FAKE, lse=FAKE)
+    p.update(kw)
+    st = rra.lib().ls_lse_merge(p["num_parts"], p["rows"], p["head_dim"], p["po"], p["pm"], p["pl"],
+                                p["o"], p["lse"], None)
+    assert st == status
+
+
+def test_timing_read_unknown_kernel_is_empty():
+    rra.ls_timing_reset()
+    assert rra.ls_timing_read("no_such_kernel") == (0, 0.0)

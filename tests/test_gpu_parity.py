@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle,
+element by element, at sizes the oracle finishes in seconds that still span
+several tiles and ragged tails, plus the method's degenerate cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from replay_inputs import (SPLIT_BLOCK_CYCLIC, SPLIT_CONTIGUOUS, TINY, ReplayShape, logical_prompt,
+                           make_inputs, scatter_prompt)
+from response_replay_attention_amd import PromptCache, replay_backward, replay_forward
+from tests.parity import assert_close, assert_lse_close, to_np
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    TINY,  # 6 q / 1 kv heads, d 128, prompt 2048, response 128, 8 splits
+    ReplayShape("ragged_d256_cyclic", 24, 4, 256, 5 * 256 + 77, 200, 3, SPLIT_BLOCK_CYCLIC, 1, extra_phys_pages=3),
+    ReplayShape("ragged_d128_cyclic2", 6, 2, 128, 9 * 256 + 1, 45, 4, SPLIT_BLOCK_CYCLIC, 2, extra_phys_pages=2),
+    ReplayShape("no_prompt", 12, 2, 256, 0, 77, 2),
+    ReplayShape("one_row", 24, 4, 256, 3 * 256, 1, 2),
+    ReplayShape("empty_splits", 6, 1, 128, 4 * 256, 64, 6),
+    ReplayShape("chunked_single_split", 6, 1, 128, 64 * 256, 128, 1),
+    ReplayShape("gqa24x4_d256_p4096_r256_s8", 24, 4, 256, 16 * 256, 256, 8),
+]
+
+
+def run_hip(shape: ReplayShape, inp, num_splits=None, policy=None, block_pages=None):
+    cache = PromptCache(inp["k_pool"], inp["v_pool"], shape.prompt_len, inp["l2p"],
+                        num_splits or shape.num_splits,
+                        shape.policy if policy is None else policy,
+                        block_pages or shape.block_pages)
+    fwd = replay_forward(cache, inp["q"], inp["k_resp"], inp["v_resp"], shape.scale)
+    dq, dk, dv = replay_backward(cache, inp["q"], inp["k_resp"], inp["v_resp"], fwd.o, fwd.lse,
+                                 inp["d_o"], shape.scale)
+    torch.cuda.synchronize()
+    return cache, fwd, dq, dk, dv
+
+
+def oracle_inputs(shape: ReplayShape, inp):
+    kp = logical_prompt(inp["k_pool"], inp["l2p"], shape.prompt_len).cpu()
+    vp = logical_prompt(inp["v_pool"], inp["l2p"], shape.prompt_len).cpu()
+    return (inp["q"].cpu(), kp, vp, inp["k_resp"].cpu(), inp["v_resp"].cpu(), inp["d_o"].cpu())
+
+
+# outputs far from the N(0,1) scale of the five workloads: relative bounds only
+RELATIVE_ONLY = {"no_prompt"}
+
+
+def check_all(shape, inp, fwd, dq, dk, dv, contract=None):
+    contract = (shape.name not in RELATIVE_ONLY) if contract is None else contract
+    q, kp, vp, kr, vr, do = oracle_inputs(shape, inp)
+    dq_r, dk_r, dv_r, o_r, lse_r = oracle.replay_backward(q, kp, vp, kr, vr, do, shape.scale)
+    out = {
+        "o": assert_close("O", fwd.o, o_r, contract),
+        "lse": assert_lse_close("LSE", fwd.lse, lse_r),
+        "dq": assert_close("dQ", dq, dq_r, contract),
+        "dk": assert_close("dK_r", dk, dk_r, contract),
+        "dv": assert_close("dV_r", dv, dv_r, contract),
+    }
+    return out
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: s.name)
+def test_forward_backward_match_oracle(shape):
+    print(f"case {shape.name}", flush=True)
+    inp = make_inputs(shape, seed=11, device="cuda")
+    _, fwd, dq, dk, dv = run_hip(shape, inp)
+    check_all(shape, inp, fwd, dq, dk, dv)
+
+
+@pytest.mark.parametrize("shape", [TINY, SMALL[1]], ids=lambda s: s.name)
+def test_split_partials_match_oracle(shape):
+    """Each split's (m, l, o) is the plain statistic of its own pages (compared
+    through m + ln l, which is what the pair defines), and the response part is
+    the causal block."""
+    inp = make_inputs(shape, seed=5, device="cuda")
+    cache, fwd, *_ = run_hip(shape, inp)
+    q, kp, vp, kr, vr, _ = oracle_inputs(shape, inp)
+    g = shape.hq // shape.hkv
+    R = shape.resp_len
+    offs = cache.split_offsets_host
+    for c in range(shape.num_splits + 1):
+        for h in range(shape.hq):
+            kv = h // g
+            if c < shape.num_splits:
+                pages = cache.order[offs[c]:offs[c + 1]]
+                keys = [p * 256 + t for p in pages for t in range(256) if p * 256 + t < shape.prompt_len]
+                m, l_, o = oracle.partial_stats(q[h], kp[kv][keys], vp[kv][keys], shape.scale)
+            else:
+                vis = np.arange(R)[None, :] <= np.arange(R)[:, None]
+                m, l_, o = oracle.partial_stats(q[h], kr[kv], vr[kv], shape.scale, visible=vis)
+            gm = to_np(fwd.part_m[c, h])
+            gl = to_np(fwd.part_l[c, h])
+            empty = l_ == 0
+            assert np.all(gl[empty] == 0) and np.all(np.isneginf(gm[empty]))
+            if (~empty).any():
+                assert_lse_close(f"part{c} h{h} lse", gm[~empty] + np.log(gl[~empty]),
+                                 m[~empty] + np.log(l_[~empty]))
+                assert_close(f"part{c} h{h} o", to_np(fwd.part_o[c, h])[~empty], o[~empty])
+            assert np.all(to_np(fwd.part_o[c, h])[empty] == 0)
+
+
+def test_peaked_scores():
+    """Q scaled by 4: scores ~ N(0, 16) exercise the max shift with O(1) outputs."""
+    shape = SMALL[7]
+    inp = make_inputs(shape, seed=3, device="cuda", q_mult=4.0)
+    _, fwd, dq, dk, dv = run_hip(shape, inp)
+    check_all(shape, inp, fwd, dq, dk, dv, contract=False)
+
+
+def test_late_dominant_key_triggers_exact_recompute():
+    """One prompt key late in the prompt scores ~90 log2-units above the first
+    block's max; the forward must detect it and still be exact."""
+    shape = ReplayShape("dominant_key", 6, 1, 128, 8 * 256, 32, 2)
+    inp = make_inputs(shape, seed=7, device="cuda")
+    u = torch.randn(128, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).float()
+    q = (u[None, None, :] + 0.1 * inp["q"].float().cpu()).to(torch.bfloat16)
+    inp["q"] = q.cuda()
+    kl = logical_prompt(inp["k_pool"], inp["l2p"], shape.prompt_len).cpu()
+    kl[0, 1500] = (4.0 * u).to(torch.bfloat16)   # split 1 of 2, far from its first block
+    inp["k_pool"] = scatter_prompt(kl.cuda(), inp["l2p"], shape.num_phys_pages, fill=inp["k_pool"])
+    _, fwd, dq, dk, dv = run_hip(shape, inp)
+    q, kp, vp, kr, vr, do = oracle_inputs(shape, inp)
+    dq_r, dk_r, dv_r, o_r, lse_r = oracle.replay_backward(q, kp, vp, kr, vr, do, shape.scale)
+    assert float(lse_r.min()) > 40.0          # the dominant key really dominates
+    assert_close("O", fwd.o, o_r, contract=False)
+    assert_lse_close("LSE", fwd.lse, lse_r)
+    # the softmax is one-hot, so the true gradients are ~1e-17: what remains
+    # is rounding noise of a vanishing quantity, bounded in absolute terms
+    for name, got, ref in (("dQ", dq, dq_r), ("dK_r", dk, dk_r), ("dV_r", dv, dv_r)):
+        assert float(np.abs(to_np(got) - ref).max()) <= 1e-4, name
+
+
+def test_zero_query_closed_form():
+    """Q = 0: LSE_i = ln(P + i + 1) and O_i is the mean of the visible values."""
+    shape = SMALL[1]
+    inp = make_inputs(shape, seed=2, device="cuda", q_zero=True)
+    _, fwd, *_ = run_hip(shape, inp)
+    P, R = shape.prompt_len, shape.resp_len
+    vp = to_np(logical_prompt(inp["v_pool"], inp["l2p"], P))
+    vr = to_np(inp["v_resp"])
+    want_lse = np.log(P + np.arange(R) + 1.0)
+    g = shape.hq // shape.hkv
+    for h in range(shape.hq):
+        kv = h // g
+        assert_lse_close(f"lse h{h}", fwd.lse[h], want_lse)
+        csum = vp[kv].sum(0)[None, :] + np.cumsum(vr[kv], axis=0)
+        assert_close(f"o h{h}", fwd.o[h], csum / (P + np.arange(R) + 1.0)[:, None])
+
+
+def test_constant_values_give_constant_output():
+    """V = c everywhere: O = c (P enters the MFMA rounded to bf16 while the
+    normaliser is the unrounded sum, so the match is within tolerance)."""
+    shape = SMALL[2]
+    inp = make_inputs(shape, seed=4, device="cuda", v_const=0.625)
+    _, fwd, *_ = run_hip(shape, inp)
+    assert_close("O", fwd.o, np.full(tuple(fwd.o.shape), 0.625))
+    assert float((fwd.o.float() - 0.625).abs().max()) <= 2 ** -8
+
+
+def test_split_policy_invariance():
+    """Any page partition gives the same result up to rounding; each is checked
+    against the oracle and against each other."""
+    shape = SMALL[7]
+    inp = make_inputs(shape, seed=9, device="cuda")
+    results = []
+    for ns, pol, blk in ((1, SPLIT_CONTIGUOUS, 1), (3, SPLIT_CONTIGUOUS, 1), (8, SPLIT_BLOCK_CYCLIC, 1),
+                         (5, SPLIT_BLOCK_CYCLIC, 3), (16, SPLIT_CONTIGUOUS, 1)):
+        _, fwd, dq, dk, dv = run_hip(shape, inp, num_splits=ns, policy=pol, block_pages=blk)
+        check_all(shape, inp, fwd, dq, dk, dv)
+        results.append((fwd.o.float(), fwd.lse, dq))
+    for o, lse, dq in results[1:]:
+        assert_close("O vs S=1", o, results[0][0])
+        assert_lse_close("LSE vs S=1", lse, results[0][1])
+        assert_close("dQ vs S=1", dq, results[0][2])
+
+
+def test_page_placement_does_not_change_bits():
+    """The same logical prompt under the identity map and under a random map
+    gives bitwise identical outputs: the page table only changes addresses."""
+    shape = SMALL[7]
+    a = make_inputs(shape, seed=21, device="cuda", identity_pages=True)
+    b = dict(a)
+    perm = torch.randperm(shape.num_phys_pages, generator=torch.Generator().manual_seed(3))[: shape.num_pages]
+    b["l2p"] = perm.to(torch.int32)
+    for name in ("k_pool", "v_pool"):
+        logical = logical_prompt(a[name], a["l2p"], shape.prompt_len)
+        b[name] = scatter_prompt(logical, b["l2p"], shape.num_phys_pages, fill=a[name])
+    ra = run_hip(shape, a)
+    rb = run_hip(shape, b)
+    assert torch.equal(ra[1].o, rb[1].o) and torch.equal(ra[1].lse, rb[1].lse)
+    for x, y in zip(ra[2:], rb[2:]):
+        assert torch.equal(x, y)
+
+
+def test_deterministic_and_pools_untouched():
+    shape = SMALL[1]
+    inp = make_inputs(shape, seed=13, device="cuda")
+    kp0, vp0 = inp["k_pool"].clone(), inp["v_pool"].clone()
+    r1 = run_hip(shape, inp)
+    r2 = run_hip(shape, inp)
+    assert torch.equal(r1[1].o, r2[1].o) and torch.equal(r1[1].lse, r2[1].lse)
+    assert torch.equal(r1[1].part_o, r2[1].part_o)
+    for x, y in zip(r1[2:], r2[2:]):
+        assert torch.equal(x, y)
+    assert torch.equal(inp["k_pool"], kp0) and torch.equal(inp["v_pool"], vp0)
+
+
+def test_no_prompt_gradient_output_exists():
+    """The stopgrad is structural: the backward returns exactly dQ, dK_r, dV_r
+    (response-sized), and nothing shaped like the prompt."""
+    shape = SMALL[5]
+    inp = make_inputs(shape, seed=1, device="cuda")
+    cache, fwd, dq, dk, dv = run_hip(shape, inp)
+    assert dq.shape == inp["q"].shape
+    assert dk.shape == dv.shape == inp["k_resp"].shape
