@@ -104,15 +104,15 @@ def replay_forward(q, k_prompt, v_prompt, k_resp, v_resp, scale: float,
     n = rows.shape[1]
     o = np.zeros((hq, n, d))
     lse = np.zeros((hq, n))
-    for h in range(hq):
-        kv = h // g
+    for kv in range(hkv):
         vcat = np.concatenate([vp[kv], vr[kv]], axis=0)
-        for s0 in range(0, n, row_block):
-            ib = rows[h, s0:s0 + row_block]
-            x = _score_rows(q[h, ib], kp[kv], kr[kv], ib, scale)
-            p, l_ = _softmax_rows(x)
-            o[h, s0:s0 + len(ib)] = p @ vcat
-            lse[h, s0:s0 + len(ib)] = l_
+        for h in range(kv * g, (kv + 1) * g):
+            for s0 in range(0, n, row_block):
+                ib = rows[h, s0:s0 + row_block]
+                x = _score_rows(q[h, ib], kp[kv], kr[kv], ib, scale)
+                p, l_ = _softmax_rows(x)
+                o[h, s0:s0 + len(ib)] = p @ vcat
+                lse[h, s0:s0 + len(ib)] = l_
     return o, lse
 
 
@@ -138,24 +138,24 @@ def replay_backward(q, k_prompt, v_prompt, k_resp, v_resp, d_o, scale: float,
     dvr = np.zeros((hkv, r, d))
     o_all = np.zeros((hq, n, d))
     lse_all = np.zeros((hq, n))
-    for h in range(hq):
-        kv = h // g
+    for kv in range(hkv):
         kcat = np.concatenate([kp[kv], kr[kv]], axis=0)
         vcat = np.concatenate([vp[kv], vr[kv]], axis=0)
-        for s0 in range(0, n, row_block):
-            ib = rows[h, s0:s0 + row_block]
-            qb, dob = q[h, ib], do[h, ib]
-            x = _score_rows(qb, kp[kv], kr[kv], ib, scale)
-            p, l_ = _softmax_rows(x)
-            o = p @ vcat
-            dd = np.sum(dob * o, axis=1, keepdims=True)      # D = <dO, O>
-            dp = dob @ vcat.T                                # dP_j = <dO, V_j>
-            ds = p * (dp - dd)                               # masked keys: p = 0
-            dq[h, s0:s0 + len(ib)] = scale * (ds @ kcat)
-            dkr[kv] += scale * (ds[:, p_len:].T @ qb)
-            dvr[kv] += p[:, p_len:].T @ dob
-            o_all[h, s0:s0 + len(ib)] = o
-            lse_all[h, s0:s0 + len(ib)] = l_
+        for h in range(kv * g, (kv + 1) * g):
+            for s0 in range(0, n, row_block):
+                ib = rows[h, s0:s0 + row_block]
+                qb, dob = q[h, ib], do[h, ib]
+                x = _score_rows(qb, kp[kv], kr[kv], ib, scale)
+                p, l_ = _softmax_rows(x)
+                o = p @ vcat
+                dd = np.sum(dob * o, axis=1, keepdims=True)      # D = <dO, O>
+                dp = dob @ vcat.T                                # dP_j = <dO, V_j>
+                ds = p * (dp - dd)                               # masked keys: p = 0
+                dq[h, s0:s0 + len(ib)] = scale * (ds @ kcat)
+                dkr[kv] += scale * (ds[:, p_len:].T @ qb)
+                dvr[kv] += p[:, p_len:].T @ dob
+                o_all[h, s0:s0 + len(ib)] = o
+                lse_all[h, s0:s0 + len(ib)] = l_
     return dq, dkr, dvr, o_all, lse_all
 
 

@@ -154,6 +154,20 @@ def make_inputs(shape: ReplayShape, seed: int, device="cpu", *,
     return out
 
 
+def make_response(shape: ReplayShape, seed: int, device="cpu") -> Dict[str, torch.Tensor]:
+    """Only the response side of a problem (``q``, ``k_resp``, ``v_resp``,
+    ``d_o``), drawn exactly as :func:`make_inputs` draws them: used for the
+    members of a group that share one prompt pool."""
+    H, Hk, d, R = shape.hq, shape.hkv, shape.head_dim, shape.resp_len
+    dev = torch.device(device)
+    return {
+        "q": _randn_bf16((H, R, d), _gen(seed, _T_Q, dev), dev),
+        "k_resp": _randn_bf16((Hk, R, d), _gen(seed, _T_KR, dev), dev),
+        "v_resp": _randn_bf16((Hk, R, d), _gen(seed, _T_VR, dev), dev),
+        "d_o": _randn_bf16((H, R, d), _gen(seed, _T_DO, dev), dev),
+    }
+
+
 def logical_prompt(pool: torch.Tensor, l2p: torch.Tensor, prompt_len: int,
                    kv_heads: Optional[List[int]] = None) -> torch.Tensor:
     """Gather the pool back into logical order: ``[Hkv, prompt_len, d]`` (same
