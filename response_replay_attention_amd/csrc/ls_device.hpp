@@ -68,29 +68,37 @@ __device__ __forceinline__ int swz(int row, int col) {
   return row * D + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
 }
 
-// ---- 32x32x16 tiles (used where a wave owns 32 query rows)
+// ---- 32x32x16 tiles (a wave owns 32 query rows)
 // Lane-dependent parts of the swizzled LDS addresses, computed once per kernel
 // so that every tile access inside the key loop is "base register +
 // compile-time immediate" (otherwise the compiler hoists one address register
-// per access out of the loop).
-//   row operand, k-step kk (16-byte chunk 2*kk + hf of row lq):
-//     lq*D + 8*((2*kk + hf) ^ (lq & 15))          = rb[kk & 7] + 128*(kk >> 3)
-//   column gather, element t of (ks, mt) (row kperm(ks,hf,t), column 32*mt + lq),
-//   with M = mt ^ (2*(t >> 2)):
-//     = cb[t & 3][M & 1] + (16*ks + 8*(t >> 2) + (t & 3))*D + 32*M
+// per access out of the loop and runs out of registers).
+//
+// Row operand of k-step kk: row lq, 16-byte chunk 2*kk + hf:
+//     lq*D + 8*((2*kk + hf) ^ (lq & 15))  =  rb[kk & 7] + 128*(kk >> 3)
+//
+// Column operand of (ks, mt): column 32*mt + lq at rows kperm(ks, hf, 0..7),
+// read with ds_read_b64_tr_b16.  That instruction works on groups of 16 lanes:
+// lane i of a group receives, as element e, the 16-bit word (i & 3) of the
+// 8 bytes addressed by lane 4*e + (i >> 2) of the same group.  So lane
+// L = 4*e' + j' (L = lane & 15) supplies the address of row
+// kperm(ks, hf, 4*c + e') and columns 32*mt + 16*((lane >> 4) & 1) + 4*j' + [0,4),
+// and after two reads (c = 0, 1) every lane holds its column at the 8 rows.
+// With the swizzle that address is
+//     tb[mt & 1] + (16*ks + 8*c)*D + 64*(((mt >> 1) & 1) ^ c) + 128*(mt >> 2).
 template <int D>
 struct Lanes32 {
   int rb[8];
-  int cb[4][2];
+  int tb[2];
   __device__ __forceinline__ Lanes32(int hf, int lq) {
 #pragma unroll
     for (int k7 = 0; k7 < 8; ++k7) rb[k7] = lq * D + 8 * ((2 * k7 + hf) ^ (lq & 15));
+    const int L = lq & 15, g1 = (lq >> 4) & 1;
+    const int b0 = ((L >> 1) ^ (L >> 2)) & 1;
+    const int b1 = (g1 ^ (L >> 3)) & 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int base = 4 * hf * D + 8 * ((lq >> 3) ^ j) + (lq & 7);
-      cb[j][0] = base + 32 * hf;
-      cb[j][1] = base - 32 * hf;
-    }
+    for (int p = 0; p < 2; ++p)
+      tb[p] = (4 * hf + (L >> 2)) * D + 8 * (b0 + 2 * b1 + 4 * (p ^ hf)) + 4 * (L & 1);
   }
   // 16-byte row operand of k-step kk: row lq, elements [16*kk + 8*hf, +8).
   __device__ __forceinline__ bf16x8 row8(const uint16_t* tile, int kk) const {
@@ -98,12 +106,25 @@ struct Lanes32 {
   }
   // 8 values of column 32*mt + lq at rows kperm(ks, hf, 0..7).
   __device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int ks, int mt) const {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint16_t* base = tile + tb[mt & 1] + 16 * ks * D + 128 * (mt >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + 64 * ((mt >> 1) & 1)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + 8 * D + 64 * (((mt >> 1) & 1) ^ 1)));
+    const s16x4 v[2] = {lo, hi};
     u16x8 r;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int M = mt ^ (2 * (t >> 2));
-      r[t] = tile[cb[t & 3][M & 1] + (16 * ks + 8 * (t >> 2) + (t & 3)) * D + 32 * M];
-    }
+    for (int t = 0; t < 8; ++t) r[t] = (unsigned short)v[t >> 2][t & 3];
+    return __builtin_bit_cast(bf16x8, r);
+  }
+  // Reference gather with one 16-bit LDS read per element (same result as col8).
+  __device__ __forceinline__ bf16x8 col8_scalar(const uint16_t* tile, int ks, int mt,
+                                                int hf, int lq) const {
+    u16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = tile[swz<D>(kperm(ks, hf, t), 32 * mt + lq)];
     return __builtin_bit_cast(bf16x8, r);
   }
 };
