@@ -59,13 +59,22 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 }
 
 // ---- LDS tiles of 32 rows x D bf16 (one K or V block), unpadded.
-// 16-byte chunk c of row r is stored at chunk position c ^ (r & 15).  With this
-// swizzle the row-operand reads (16 B per lane, 32 rows) and the column
-// gathers below hit distinct banks, and a wave can fill 1 KB of the tile with
-// one direct global->LDS copy.
+// 16-byte chunk c of row r is stored at chunk position c ^ swf(r), where swf
+// swaps the two 2-bit halves of r & 15.  Rows are 512 B (d = 256) or 256 B
+// apart, so without a swizzle every row starts in the same LDS bank; with this
+// one, on the 64 x 4-byte banks of gfx950,
+//   * a row-operand read (16 B per lane, 16 consecutive rows per bank pass)
+//     hits 16 distinct 16-byte bank groups, and
+//   * a transpose read (8 B per lane; each 32-lane pass reads the same 64-byte
+//     column range of 4 consecutive rows, for 2 lane halves) lands the 4 rows
+//     in 4 distinct 64-byte bank groups,
+// so both are free of bank conflicts; and a wave can still fill 1 KB of the
+// tile with one direct global->LDS copy.
+__device__ __forceinline__ constexpr int swf(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
-  return row * D + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
+  return row * D + ((((col >> 3) ^ swf(row))) << 3) + (col & 7);
 }
 
 // ---- 32x32x16 tiles (a wave owns 32 query rows)
@@ -75,30 +84,31 @@ __device__ __forceinline__ int swz(int row, int col) {
 // per access out of the loop and runs out of registers).
 //
 // Row operand of k-step kk: row lq, 16-byte chunk 2*kk + hf:
-//     lq*D + 8*((2*kk + hf) ^ (lq & 15))  =  rb[kk & 7] + 128*(kk >> 3)
+//     lq*D + 8*((2*kk + hf) ^ swf(lq))  =  rb[kk & 7] + 128*(kk >> 3)
 //
 // Column operand of (ks, mt): column 32*mt + lq at rows kperm(ks, hf, 0..7),
 // read with ds_read_b64_tr_b16.  That instruction works on groups of 16 lanes:
 // lane i of a group receives, as element e, the 16-bit word (i & 3) of the
 // 8 bytes addressed by lane 4*e + (i >> 2) of the same group.  So lane
-// L = 4*e' + j' (L = lane & 15) supplies the address of row
-// kperm(ks, hf, 4*c + e') and columns 32*mt + 16*((lane >> 4) & 1) + 4*j' + [0,4),
-// and after two reads (c = 0, 1) every lane holds its column at the 8 rows.
-// With the swizzle that address is
-//     tb[mt & 1] + (16*ks + 8*c)*D + 64*(((mt >> 1) & 1) ^ c) + 128*(mt >> 2).
+// L = 4*e' + j' (L = lane & 15) supplies, for read c (elements 4c..4c+3), the
+// address of row 16*ks + 8*c + 4*hf + e' and columns
+// 32*mt + 16*((lane >> 4) & 1) + 4*j' + [0, 4).  Under the swizzle
+// (swf of that row = 4*e' + 2*c + hf) this is
+//     tb[c][mt & 3] + (16*ks + 8*c)*D + 128*(mt >> 2).
 template <int D>
 struct Lanes32 {
   int rb[8];
-  int tb[2];
+  int tb[2][4];
   __device__ __forceinline__ Lanes32(int hf, int lq) {
 #pragma unroll
-    for (int k7 = 0; k7 < 8; ++k7) rb[k7] = lq * D + 8 * ((2 * k7 + hf) ^ (lq & 15));
-    const int L = lq & 15, g1 = (lq >> 4) & 1;
-    const int b0 = ((L >> 1) ^ (L >> 2)) & 1;
-    const int b1 = (g1 ^ (L >> 3)) & 1;
+    for (int k7 = 0; k7 < 8; ++k7) rb[k7] = lq * D + 8 * ((2 * k7 + hf) ^ swf(lq));
+    const int L = lq & 15, g1 = (lq >> 4) & 1, e = L >> 2;
+    const int b0 = ((L >> 1) & 1) ^ hf;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      tb[p] = (4 * hf + (L >> 2)) * D + 8 * (b0 + 2 * b1 + 4 * (p ^ hf)) + 4 * (L & 1);
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int m3 = 0; m3 < 4; ++m3)
+        tb[c][m3] = (4 * hf + e) * D + 8 * (b0 + 2 * (g1 ^ c) + 4 * (m3 ^ e)) + 4 * (L & 1);
   }
   // 16-byte row operand of k-step kk: row lq, elements [16*kk + 8*hf, +8).
   __device__ __forceinline__ bf16x8 row8(const uint16_t* tile, int kk) const {
@@ -108,66 +118,14 @@ struct Lanes32 {
   __device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int ks, int mt) const {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const uint16_t* base = tile + tb[mt & 1] + 16 * ks * D + 128 * (mt >> 2);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(base + 64 * ((mt >> 1) & 1)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(base + 8 * D + 64 * (((mt >> 1) & 1) ^ 1)));
+    const uint16_t* base = tile + 16 * ks * D + 128 * (mt >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + tb[0][mt & 3]));
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * D + tb[1][mt & 3]));
     const s16x4 v[2] = {lo, hi};
     u16x8 r;
 #pragma unroll
     for (int t = 0; t < 8; ++t) r[t] = (unsigned short)v[t >> 2][t & 3];
-    return __builtin_bit_cast(bf16x8, r);
-  }
-  // Reference gather with one 16-bit LDS read per element (same result as col8).
-  __device__ __forceinline__ bf16x8 col8_scalar(const uint16_t* tile, int ks, int mt,
-                                                int hf, int lq) const {
-    u16x8 r;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) r[t] = tile[swz<D>(kperm(ks, hf, t), 32 * mt + lq)];
-    return __builtin_bit_cast(bf16x8, r);
-  }
-};
-
-// ---- 16x16x32 tiles (used where a wave owns 48 query rows)
-// v_mfma_f32_16x16x32_bf16 layouts (lane l, group g4 = l/16, lc = l%16):
-//   A: row lc, k = 8*g4 + t;  B: column lc, k = 8*g4 + t;
-//   accumulator register r: row 4*g4 + r, column lc.
-// Two 16-row accumulator tiles (rows 0-15, 16-31) fed back as one 32-deep B
-// operand: element t of lane group g4 is row kperm16(g4, t).
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ constexpr int kperm16(int g4, int t) {
-  return 16 * (t >> 2) + 4 * g4 + (t & 3);
-}
-//   row operand, key tile kt, k-step kk (16-byte chunk 4*kk + g4 of row 16*kt + lc):
-//     (16*kt + lc)*D + 8*((4*kk + g4) ^ lc)      = rb[kk & 3] + 16*kt*D + 128*(kk >> 2)
-//   column gather, element t of head_dim tile mt (row kperm16(g4,t), column 16*mt + lc):
-//     = cb[t & 1][(mt >> 1) & 3] + (16*(t >> 2) + (t & 3))*D
-//       + 16*((mt & 1) ^ ((t >> 1) & 1)) + 128*(mt >> 3)
-template <int D>
-struct Lanes16 {
-  int rb[4];
-  int cb[2][4];
-  __device__ __forceinline__ Lanes16(int g4, int lc) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) rb[k] = lc * D + 8 * ((4 * k + g4) ^ lc);
-#pragma unroll
-    for (int t0 = 0; t0 < 2; ++t0)
-#pragma unroll
-      for (int m2 = 0; m2 < 4; ++m2)
-        cb[t0][m2] = 4 * g4 * D + (lc & 7) + 8 * ((lc >> 3) ^ t0) + 32 * (m2 ^ g4);
-  }
-  __device__ __forceinline__ bf16x8 row8(const uint16_t* tile, int kt, int kk) const {
-    return ld_bf16x8(tile + rb[kk & 3] + 16 * kt * D + 128 * (kk >> 2));
-  }
-  __device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int mt) const {
-    u16x8 r;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      r[t] = tile[cb[t & 1][(mt >> 1) & 3] + (16 * (t >> 2) + (t & 3)) * D +
-                  16 * ((mt & 1) ^ ((t >> 1) & 1)) + 128 * (mt >> 3)];
     return __builtin_bit_cast(bf16x8, r);
   }
 };
@@ -189,7 +147,7 @@ __device__ __forceinline__ void tile_load_async(uint16_t* tile, const uint16_t* 
     const int blk = wave * NIW + j;
     const int e = blk * 512 + 8 * lane;           // element offset this lane fills
     const int row = e / D;
-    const int c = ((e % D) >> 3) ^ (row & 15);    // logical chunk stored there
+    const int c = ((e % D) >> 3) ^ swf(row);       // logical chunk stored there
     const int rr = row < nvalid ? row : nvalid - 1;
     __builtin_amdgcn_global_load_lds(g + (size_t)rr * D + c * 8, (lds_ptr_t)(tile + blk * 512),
                                      16, 0, 0);
