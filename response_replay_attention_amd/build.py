@@ -55,6 +55,9 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    # resolve every symbol now, so a missing kernel launch stub fails the build
+    import ctypes
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -132,96 +132,249 @@ struct Lanes32 {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Asynchronous copy of a [32][D] bf16 block at `g` (row stride D) into an LDS
-// tile, spread over the NW waves of the workgroup (global_load_lds_dwordx4:
-// lane i of a wave instruction lands at LDS base + 16*i).  Rows >= nvalid
-// (nvalid >= 1) re-read row nvalid-1, so the tile always holds finite data;
-// callers mask those rows.  Completion: s_waitcnt vmcnt(0) + barrier.
+// Asynchronous copies of [32][D] bf16 blocks (row stride D) into LDS tiles,
+// spread over the NW waves of the workgroup with global_load_lds_dwordx4 (lane
+// i of a wave instruction lands at LDS base + 16*i; the probe of this
+// instruction confirmed the mapping).  Each lane's source offset inside a block
+// is fixed, so it is computed once.  Rows >= nvalid (1 <= nvalid < 32) re-read
+// row nvalid-1, so a tile always holds finite data; callers mask those rows.
+// Completion: s_waitcnt vmcnt + barrier.
+template <int D, int NW = 4>
+struct TileLoader {
+  static constexpr int NIW = (kBN * D * 2 / 1024) / NW;  // wave instructions per block
+  static_assert(NIW * NW * 1024 == kBN * D * 2, "tile must split evenly over the waves");
+  int off[NIW];  // element offset of this lane's 16 bytes in the source block
+  int row[NIW];
+  int blk0;
+  __device__ __forceinline__ TileLoader(int wave, int lane) : blk0(wave * NIW) {
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int e = (blk0 + j) * 512 + 8 * lane;  // element position this lane fills
+      row[j] = e / D;
+      off[j] = row[j] * D + ((((e % D) >> 3) ^ swf(row[j])) << 3);
+    }
+  }
+  __device__ __forceinline__ void load(uint16_t* tile, const uint16_t* g, int nvalid) const {
+    if (nvalid >= kBN) {
+#pragma unroll
+      for (int j = 0; j < NIW; ++j)
+        __builtin_amdgcn_global_load_lds(g + off[j], (lds_ptr_t)(tile + (blk0 + j) * 512), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NIW; ++j) {
+        const int shift = row[j] < nvalid ? 0 : (nvalid - 1 - row[j]) * D;
+        __builtin_amdgcn_global_load_lds(g + off[j] + shift, (lds_ptr_t)(tile + (blk0 + j) * 512),
+                                         16, 0, 0);
+      }
+    }
+  }
+};
+
+// Free-function form of TileLoader::load.  Kernels call this rather than the
+// member from inside lambdas: the HIP front end (ROCm 7.2 clang) silently drops
+// the host launch stub of some kernel template instantiations when a lambda in
+// the kernel calls a member function of a captured TileLoader.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile(const TileLoader<D, NW>& t, uint16_t* tile,
+                                          const uint16_t* g, int nvalid) {
+  t.load(tile, g, nvalid);
+}
+
+// One-shot form of TileLoader::load (for kernels that load few tiles).
 template <int D, int NW = 4>
 __device__ __forceinline__ void tile_load_async(uint16_t* tile, const uint16_t* g, int nvalid,
                                                 int wave, int lane) {
-  constexpr int NIW = (kBN * D * 2 / 1024) / NW;  // wave instructions per wave
+  const TileLoader<D, NW> tl(wave, lane);
+  tl.load(tile, g, nvalid);
+}
+
+// Block copies through the buffer path: buffer_load_dwordx4 ... lds with a
+// raw descriptor whose base is the block's first row (uniform, in SGPRs) and a
+// per-lane byte offset that never changes, so a copy costs no per-lane address
+// arithmetic.  The descriptor's record count is the block's valid bytes:
+// reads past it return zero (hardware range check), which keeps the tail rows
+// of a partial block finite without clamping.  Lane i of an instruction lands
+// at M0 + 16*i.
+//
+// The copies are issued from inline asm on purpose: the compiler's own
+// tracking of LDS DMA cannot tell the stages of a ring apart and makes reads
+// of one stage wait for copies still in flight into another.  Ordering is
+// explicit instead: a copy into a stage is issued only after a ring_barrier
+// that follows the last read of that stage, and a stage is read only after a
+// ring_barrier whose vmcnt covers its copy.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 block_desc(const void* base, unsigned nbytes) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = (int)(uint32_t)addr;
+  r.y = (int)((addr >> 32) & 0xffffu);  // stride 0: raw buffer, byte records
+  r.z = (int)nbytes;
+  r.w = 0x00020000;                      // 32-bit data format, no swizzle
+  return r;
+}
+
+// one wave instruction: 64 lanes x 16 bytes from desc+voff into LDS at lds
+// (M0 is saved and restored around the copy)
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds, int voff, i32x4 desc) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(desc));
+}
+
+template <int D, int NW = 4>
+struct BlockLoader {
+  static constexpr int NIW = (kBN * D * 2 / 1024) / NW;  // wave instructions per block
   static_assert(NIW * NW * 1024 == kBN * D * 2, "tile must split evenly over the waves");
+  int voff[NIW];  // byte offset of this lane's 16 bytes inside the source block
+  int lds0;       // byte offset of this wave's first 1 KB piece inside a tile (uniform)
+  __device__ __forceinline__ BlockLoader(int wave, int lane)
+      : lds0(__builtin_amdgcn_readfirstlane(wave) * NIW * 1024) {
 #pragma unroll
-  for (int j = 0; j < NIW; ++j) {
-    const int blk = wave * NIW + j;
-    const int e = blk * 512 + 8 * lane;           // element offset this lane fills
-    const int row = e / D;
-    const int c = ((e % D) >> 3) ^ swf(row);       // logical chunk stored there
-    const int rr = row < nvalid ? row : nvalid - 1;
-    __builtin_amdgcn_global_load_lds(g + (size_t)rr * D + c * 8, (lds_ptr_t)(tile + blk * 512),
-                                     16, 0, 0);
+    for (int j = 0; j < NIW; ++j) {
+      const int e = (wave * NIW + j) * 512 + 8 * lane;  // element position this lane fills
+      const int row = e / D;
+      voff[j] = 2 * (row * D + ((((e % D) >> 3) ^ swf(row)) << 3));
+    }
   }
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+// Copy rows [0, nvalid) of the block at `src` (row stride D) into `tile`;
+// rows past nvalid arrive as zeros.
+template <int D, int NW>
+__device__ __forceinline__ void load_block(const BlockLoader<D, NW>& L, uint16_t* tile,
+                                           const uint16_t* src, int nvalid) {
+  const i32x4 desc = block_desc(src, (unsigned)(nvalid * D * 2));
+  const uint32_t base = lds_addr(tile) + L.lds0;
+#pragma unroll
+  for (int j = 0; j < BlockLoader<D, NW>::NIW; ++j) copy16_to_lds(base + j * 1024, L.voff[j], desc);
+}
+
+// Page-table entries are read through the constant address space: the tables
+// never change while a kernel runs, and a uniform load from that space becomes
+// a scalar load instead of a vector load followed by a full vmcnt wait.
+__device__ __forceinline__ int ld_table(const int32_t* t, int i) {
+  return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(t))[i];
 }
 
 // Keys seen by one work item, in blocks of kBN: either a chunk of one split's
 // prompt pages (walked through the page table) or the causal response block.
-// Page ids out of range are skipped (treated as empty), so a corrupted device
-// page table can never make a kernel read outside the pools.
+// Inside a split pages are in increasing logical order, so the only partial
+// prompt page (the last logical page, when prompt_len % 256 != 0) can only be
+// the last page of a chunk: blocks [0, nfull) need no mask, [nfull, nblocks)
+// do.  A page id out of range reads block 0 of the pool in the unmasked loop
+// and is skipped in the masked one, so a corrupted device page table gives
+// wrong numbers but never an out-of-bounds access.
 template <int D, bool RESP>
 struct KeyWalk {
   const AttnArgs& a;
-  int kv, p0, nblocks;
+  int kv, p0, nblocks, nfull;
   // unit = split*chunks + chunk (paged); rows [m0, m0 + rows) of the group
   __device__ __forceinline__ KeyWalk(const AttnArgs& args, int kv_, int unit, int m0, int rows)
-      : a(args), kv(kv_), p0(0), nblocks(0) {
+      : a(args), kv(kv_), p0(0), nblocks(0), nfull(0) {
     const int GR = (a.hq / a.hkv) * a.R;
     if (RESP) {
       const int mlast = min(m0 + rows, GR) - 1;
       const int imax = (m0 / a.R != mlast / a.R) ? a.R - 1 : mlast % a.R;
       nblocks = (imax + kBN) / kBN;
+      nfull = 0;
     } else {
       const int c = unit / a.chunks, k = unit - c * a.chunks;
-      int s0 = a.offs[c], s1 = a.offs[c + 1];
+      int s0 = ld_table(a.offs, c), s1 = ld_table(a.offs, c + 1);
       s0 = min(max(s0, 0), a.num_pages);
       s1 = min(max(s1, s0), a.num_pages);
       p0 = s0 + k * a.chunk_pages;
       const int p1 = min(s1, p0 + a.chunk_pages);
-      nblocks = max(0, p1 - p0) * (kPage / kBN);
+      const int npages = max(0, p1 - p0);
+      nblocks = npages * (kPage / kBN);
+      nfull = nblocks;
+      if (npages > 0 && (a.prompt_len % kPage) != 0 && ld_table(a.order, p1 - 1) == a.num_pages - 1)
+        nfull = nblocks - kPage / kBN;
     }
   }
-  // block b: base pointers of its K and V rows, number of valid keys, index of
-  // its first key (response mode; 0 for prompt pages)
-  __device__ __forceinline__ void src(int b, const uint16_t*& kb, const uint16_t*& vb, int& nvalid,
-                                      int& key0) const {
+  // element offset of an unmasked prompt block's first row in the pool
+  __device__ __forceinline__ size_t offset(int b) const {
+    const int lp = ld_table(a.order, p0 + b / (kPage / kBN));
+    const int tok = (b % (kPage / kBN)) * kBN;
+    if (lp >= 0 && lp < a.num_pages) {
+      const int ph = ld_table(a.l2p, lp);
+      if (ph >= 0 && ph < a.num_phys) return (((size_t)ph * a.hkv + kv) * kPage + tok) * D;
+    }
+    return 0;
+  }
+  // any block: element offset of its first row (pool or response tensors),
+  // number of valid keys (0 = skip) and, for the response, its first key index
+  __device__ __forceinline__ size_t block(int b, int& nvalid, int& key0) const {
     if (RESP) {
       key0 = b * kBN;
       nvalid = min(kBN, a.R - key0);
-      const size_t off = ((size_t)kv * a.R + key0) * D;
-      kb = a.k + off;
-      vb = a.v + off;
-    } else {
-      key0 = 0;
-      nvalid = 0;
-      kb = vb = a.k;
-      const int lp = a.order[p0 + b / (kPage / kBN)];
-      const int tok = (b % (kPage / kBN)) * kBN;
-      if (lp >= 0 && lp < a.num_pages) {
-        const int ph = a.l2p[lp];
-        if (ph >= 0 && ph < a.num_phys) {
-          const int64_t left = a.prompt_len - (int64_t)lp * kPage - tok;
-          nvalid = (int)(left < 0 ? 0 : (left > kBN ? kBN : left));
-          const size_t off = (((size_t)ph * a.hkv + kv) * kPage + tok) * D;
-          kb = a.k + off;
-          vb = a.v + off;
-        }
+      return ((size_t)kv * a.R + key0) * D;
+    }
+    key0 = 0;
+    nvalid = 0;
+    const int lp = ld_table(a.order, p0 + b / (kPage / kBN));
+    const int tok = (b % (kPage / kBN)) * kBN;
+    if (lp >= 0 && lp < a.num_pages) {
+      const int ph = ld_table(a.l2p, lp);
+      if (ph >= 0 && ph < a.num_phys) {
+        const int64_t left = a.prompt_len - (int64_t)lp * kPage - tok;
+        nvalid = (int)(left < 0 ? 0 : (left > kBN ? kBN : left));
+        return (((size_t)ph * a.hkv + kv) * kPage + tok) * D;
       }
     }
+    return 0;
   }
   // start the asynchronous copy of block b's K and V into tiles kt, vt
   __device__ __forceinline__ void issue(int b, uint16_t* kt, uint16_t* vt, int wave, int lane,
                                         int& nvalid, int& key0) const {
-    const uint16_t *kb, *vb;
-    src(b, kb, vb, nvalid, key0);
+    const size_t off = block(b, nvalid, key0);
     if (nvalid > 0) {
-      tile_load_async<D>(kt, kb, nvalid, wave, lane);
-      tile_load_async<D>(vt, vb, nvalid, wave, lane);
+      tile_load_async<D>(kt, a.k + off, nvalid, wave, lane);
+      tile_load_async<D>(vt, a.v + off, nvalid, wave, lane);
     }
   }
 };
 
-__device__ __forceinline__ void wait_async_loads() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Wait until at most N of this wave's vector-memory loads (including the
+// direct global->LDS copies) are still in flight.
+// s_waitcnt immediate for "at most N vector-memory ops in flight" (gfx9
+// encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14), with
+// expcnt and, unless LGKM0, lgkmcnt left at their maxima (no wait).
+template <int N, bool LGKM0>
+constexpr int waitcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8) | ((N >> 4) << 14);
+}
+
+// Wait until at most N of this wave's vector-memory ops are in flight.  The
+// builtin (not asm) lets the compiler see the wait, so it does not add waits
+// of its own for loads this one already covers.
+template <int N>
+__device__ __forceinline__ void wait_loads_le() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<N, false>());
+}
+
+__device__ __forceinline__ void wait_async_loads() { wait_loads_le<0>(); }
+
+// Ring-buffer handoff: wait until at most N of this wave's copies are in
+// flight and its LDS reads have returned, then meet the other waves.  No
+// fence: __syncthreads()'s workgroup release would also wait for every copy
+// still in flight, which is what the ring exists to avoid.  The barrier is an
+// asm statement with a memory clobber so that no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<N, true>());
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // acc *= alpha for an accumulator tile that lives in AGPRs.  Plain C++ would

@@ -15,24 +15,86 @@
 //     one query per lane and 16 of the block's 32 keys per lane in registers,
 //     so the softmax statistics need one exchange between lanes l and l^32;
 //   * P^T (bf16) is the B operand of O^T = V^T P^T straight from registers; the
-//     V^T operand is gathered from the row-major V tile; O^T keeps one query
-//     per lane, so the rescale and the final 1/l are per-lane scalars;
-//   * K/V blocks of 32 keys are double-buffered in LDS, filled by direct
-//     global->LDS copies issued one block ahead;
-//   * the exp2 shift is fixed at the first block's max instead of being
-//     raised as the running max grows, so no accumulator is ever rescaled; an
-//     input whose scores later exceed the shift by more than 2^32 is detected
-//     and its key range recomputed with the true max as the shift.
+//     V^T operand comes from the row-major V tile by transpose reads; O^T keeps
+//     one query per lane, so the shift and the final 1/l are per-lane scalars;
+//   * full prompt blocks stream through a 4-stage LDS ring filled by
+//     buffer->LDS copies issued three blocks ahead, and the loop is software
+//     pipelined: the softmax of block b runs on the VALU while the MFMAs
+//     compute the scores of block b+1.  Masked blocks (the partial last prompt
+//     page, the causal response block) take a simple loop of their own;
+//   * the exp2 shift is fixed at the first block's max instead of following
+//     the running max, so no accumulator is ever rescaled; an input whose
+//     scores later exceed the shift by more than 2^32 is detected and its key
+//     range recomputed with the true max as the shift.
 #include "ls_device.hpp"
 
 namespace ls {
 
+// S^T[key][query] = sum_d K[key][d] Q[query][d] for the block in tile kt.
+template <int D>
+__device__ __forceinline__ f32x16 block_scores(const Lanes32<D>& tl, const uint16_t* kt,
+                                               const bf16x8 (&qr)[D / 16]) {
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) s = mfma32(tl.row8(kt, kk), qr[kk], s);
+  return s;
+}
+
+// Softmax numerators of one block for this lane's query: x = raw scores
+// (masked ones -inf), returns P^T as two bf16 B operands (register 8*ks + e
+// is k-element e of k-step ks), adds their fp32 sum to lsum.  Pass 0 fixes the
+// shift at the first block's max and flags scores that exceed it by more than
+// 2^kShiftSlack.
+__device__ __forceinline__ void block_probs(const float (&x)[16], float s2, bool pass0,
+                                            float& mref, float& mtrue, float& lsum,
+                                            bool& unsafe, bf16x8 (&pb)[2]) {
+  float mx = x[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+  const float mb = wave_max_halves(mx) * s2;
+  mtrue = fmaxf(mtrue, mb);
+  if (pass0) {
+    mref = (mref == -kInf) ? mb : mref;
+    unsafe = unsafe || (mb > mref + kShiftSlack);
+  }
+  const float mu = (mref == -kInf) ? 0.f : mref;
+  float ls = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], s2, -mu));
+    ls += p;
+    pb[r >> 3][r & 7] = to_bf16(p);
+  }
+  lsum += ls;
+}
+
+// O^T[d][query] += sum_key V[key][d] P^T[key][query] for the block in tile vt.
+template <int D>
+__device__ __forceinline__ void block_pv(f32x16 (&acc)[D / 32], const Lanes32<D>& tl,
+                                         const uint16_t* vt, const bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma32(tl.col8(vt, ks, mt), pb[ks], acc[mt]);
+  }
+}
+
 template <int D, bool RESP>
 __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
-  constexpr int NKK = D / 16;           // 16-deep k-steps over head_dim for S
-  constexpr int NMT = D / 32;           // 32-wide head_dim tiles of O^T
-  constexpr int TILE = kBN * D;         // elements of one K or V block
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // [buf][K,V]
+  constexpr int NMT = D / 32;
+  constexpr int TILE = kBN * D;                     // elements of one K or V block
+  constexpr int NST = kStages;                      // ring depth (4)
+  constexpr int NLD = 2 * BlockLoader<D>::NIW;      // load instructions per wave per block
+  // One array per ring stage: distinct LDS objects let the compiler tell the
+  // stages apart, so a read of one stage does not wait for the copies still
+  // in flight into the others.
+  __shared__ __attribute__((aligned(1024))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
+  uint16_t* const kst[NST] = {k0, k1, k2, k3};
+  uint16_t* const vst[NST] = {v0, v1, v2, v3};
+  static_assert(NST == 4, "the ring has four stages");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, lq = lane & 31;
@@ -43,41 +105,32 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
   const int rem = w - unit * per_unit;
   const int kv = rem / a.mtiles;
   const int mtile = rem - kv * a.mtiles;
-  const int g = a.hq / a.hkv;
-  const int GR = g * a.R;
+  const int GR = (a.hq / a.hkv) * a.R;
   const int m0 = mtile * kFwdRows;
   const int m = m0 + 32 * wave + lq;     // this lane's query row within the group
   const size_t row0 = (size_t)kv * GR;
-
   const KeyWalk<D, RESP> walk(a, kv, unit, m0, kFwdRows);
   const int nblocks = walk.nblocks;
+  const int nfull = walk.nfull;          // leading blocks that need no mask
   const int slot = a.slot_base + unit;
 
-  // ---- Q (B operand): column = query m, k = 16*kk + 8*hf + e.  Rows past the
+  // Q (B operand): column = query m, k = 16*kk + 8*hf + e.  Rows past the
   // group are computed on a copy of its last row and never stored.
-  bf16x8 qr[NKK];
+  bf16x8 qr[D / 16];
   const int qi = m % a.R;
   {
     const uint16_t* qp = a.q + (row0 + min(m, GR - 1)) * D + 8 * hf;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qr[kk] = ld_bf16x8(qp + 16 * kk);
+    for (int kk = 0; kk < D / 16; ++kk) qr[kk] = ld_bf16x8(qp + 16 * kk);
   }
-
-  auto issue = [&](int b, int buf, int& nvalid, int& key0) {
-    walk.issue(b, smem + buf * 2 * TILE, smem + buf * 2 * TILE + TILE, wave, lane, nvalid, key0);
-  };
+  const Lanes32<D> tl(hf, lq);
+  const BlockLoader<D> ldr(wave, lane);
 
   f32x16 acc[NMT];
   float mref = -kInf;   // exp2 shift of this query (log2 units)
-  float mtrue = -kInf;  // running max of this query's scores
+  float mtrue = -kInf;  // running max of this query's scaled scores
   float lsum = 0.f;
-  const Lanes32<D> tl(hf, lq);
 
-  // Pass 0 fixes the shift at the first block's max and never rescales the
-  // accumulators; a score more than 2^kShiftSlack above the shift marks the
-  // pass as unsafe (fp32 overflow risk) and pass 1 redoes the key range with
-  // the true max as the shift.  Keeping the accumulators free of any VALU
-  // access inside the loop lets them stay in AGPRs.
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
@@ -86,79 +139,86 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
     lsum = 0.f;
     if (pass == 1) mref = mtrue;
     bool unsafe = false;
+    const bool pass0 = pass == 0;
 
-    int cur_nv = 0, cur_k0 = 0;
-    if (nblocks > 0) issue(0, 0, cur_nv, cur_k0);
-    wait_async_loads();
-    __syncthreads();
+    // ---- pipelined loop over the full (unmasked) blocks.  Iteration b waits
+    // for K(b+1) and V(b), starts K(b+4) and V(b+3), computes S(b+1) while
+    // turning S(b) into P(b), then accumulates V(b)^T P(b).  Every iteration
+    // issues exactly NLD loads (blocks past the range re-read block 0), so
+    // "at most two iterations' loads in flight" is a fixed vmcnt.
+    if (nfull > 0) {
+      wait_loads_le<0>();  // Q has landed (the copies below are invisible to the compiler)
+      size_t koff[NST];  // source offset (elements) of the block held by each K stage
+#define LS_ISSUE_K(j, st)                                          \
+  do {                                                             \
+    koff[st] = (j) < nfull ? walk.offset(j) : 0;                   \
+    load_block(ldr, kst[st], a.k + koff[st], kBN);       \
+  } while (0)
+#define LS_ISSUE_V(st) load_block(ldr, vst[st], a.v + koff[st], kBN)
+      LS_ISSUE_K(0, 0);
+      LS_ISSUE_K(1, 1);
+      LS_ISSUE_V(0);
+      LS_ISSUE_K(2, 2);
+      LS_ISSUE_V(1);
+      LS_ISSUE_K(3, 3);
+      LS_ISSUE_V(2);  // V(j) always goes to stage j % NST, after K(j)
+      ring_barrier<3 * NLD>();  // K(0) landed
+      f32x16 s_cur = block_scores<D>(tl, kst[0], qr);
+#define LS_FWD_STEP(ST)                                                               \
+  if (b + (ST) < nfull) {                                                             \
+    /* K(b+1), V(b) landed; stages ST (K) and ST-1 (V) are free */                  \
+    ring_barrier<2 * NLD>();                                                          \
+    LS_ISSUE_V(((ST) + NST - 1) % NST);                                               \
+    LS_ISSUE_K(b + (ST) + NST, (ST));                                                 \
+    const f32x16 s_next = block_scores<D>(tl, kst[((ST) + 1) % NST], qr);      \
+    float x[16];                                                                      \
+    for (int r = 0; r < 16; ++r) x[r] = s_cur[r];                                     \
+    bf16x8 pb[2];                                                                     \
+    block_probs(x, a.s2, pass0, mref, mtrue, lsum, unsafe, pb);                       \
+    block_pv<D>(acc, tl, vst[ST], pb);                                                      \
+    s_cur = s_next;                                                                   \
+  }
+      for (int b = 0; b < nfull; b += NST) {
+        LS_FWD_STEP(0)
+        LS_FWD_STEP(1)
+        LS_FWD_STEP(2)
+        LS_FWD_STEP(3)
+      }
+#undef LS_FWD_STEP
+#undef LS_ISSUE_V
+#undef LS_ISSUE_K
+      wait_loads_le<0>();  // drain the look-ahead loads before LDS is reused
+      __syncthreads();
+    }
 
-    // one key block; BUF is a compile-time buffer index so LDS offsets are immediates
-    auto step = [&](int b, auto buf_tag) {
-      constexpr int BUF = decltype(buf_tag)::value;
-      int nx_nv = 0, nx_k0 = 0;
-      // the other buffer was last read in block b-1, before the barrier that ended it
-      if (b + 1 < nblocks) issue(b + 1, BUF ^ 1, nx_nv, nx_k0);
-
-      if (cur_nv > 0) {
-        const uint16_t* kl = smem + BUF * 2 * TILE;
-        const uint16_t* vl = kl + TILE;
-
-        // S^T[key][query] = sum_d K[key][d] Q[query][d]
-        f32x16 s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) s = mfma32(tl.row8(kl, kk), qr[kk], s);
-
-        // scale to log2 units, mask, block max of this query (lanes l, l^32)
-        float mx = -kInf;
+    // ---- masked blocks (partial last prompt page; the causal response block)
+    for (int j = nfull; j < nblocks; ++j) {
+      int nv, key0;
+      const size_t off = walk.block(j, nv, key0);
+      if (nv > 0) {
+        load_block(ldr, k0, a.k + off, nv);
+        load_block(ldr, v0, a.v + off, nv);
+      }
+      wait_loads_le<0>();
+      __syncthreads();
+      if (nv > 0) {
+        const f32x16 s = block_scores<D>(tl, k0, qr);
+        float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = crow(r, hf);
-          bool ok = key < cur_nv;
-          if (RESP) ok = ok && (cur_k0 + key <= qi);
-          const float x = ok ? s[r] * a.s2 : -kInf;
-          s[r] = x;
-          mx = fmaxf(mx, x);
+          bool ok = key < nv;
+          if (RESP) ok = ok && (key0 + key <= qi);
+          x[r] = ok ? s[r] : -kInf;
         }
-        const float mb = wave_max_halves(mx);
-        mtrue = fmaxf(mtrue, mb);
-        if (pass == 0) {
-          if (mref == -kInf) mref = mb;
-          unsafe = unsafe || (mb > mref + kShiftSlack);
-        }
-
-        // P^T = exp2(x - m) -> bf16 B operands (register 8*ks + e -> k-element e)
         bf16x8 pb[2];
-        const float mu = (mref == -kInf) ? 0.f : mref;
-        float ls = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[r] - mu);
-          ls += p;
-          pb[r >> 3][r & 7] = to_bf16(p);
-        }
-        lsum += ls;
-
-        // O^T[d][query] += sum_key V[key][d] P^T[key][query]
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma32(tl.col8(vl, ks, mt), pb[ks], acc[mt]);
-        }
+        block_probs(x, a.s2, pass0, mref, mtrue, lsum, unsafe, pb);
+        block_pv<D>(acc, tl, v0, pb);
       }
-
-      cur_nv = nx_nv;
-      cur_k0 = nx_k0;
-      wait_async_loads();
-      __syncthreads();
-    };
-
-    for (int b = 0; b < nblocks; b += 2) {
-      step(b, IntC<0>{});
-      if (b + 1 < nblocks) step(b + 1, IntC<1>{});
+      __syncthreads();  // tiles are rewritten by the next block
     }
-    if (pass == 0 && !__syncthreads_or(unsafe ? 1 : 0)) break;
+
+    if (!pass0 || !__syncthreads_or(unsafe ? 1 : 0)) break;
   }
 
   // ---- epilogue: o = O^T / l, m in natural-log units
@@ -172,12 +232,11 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 x = read_acc4(acc[mt], r4);
         float4 v;
-        v.x = x[0] * inv;
-        v.y = x[1] * inv;
-        v.z = x[2] * inv;
-        v.w = x[3] * inv;
+        v.x = acc[mt][4 * r4 + 0] * inv;
+        v.y = acc[mt][4 * r4 + 1] * inv;
+        v.z = acc[mt][4 * r4 + 2] * inv;
+        v.w = acc[mt][4 * r4 + 3] * inv;
         *reinterpret_cast<float4*>(op + 32 * mt + 8 * r4) = v;
       }
     }

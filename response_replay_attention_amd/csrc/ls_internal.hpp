@@ -15,6 +15,7 @@ constexpr int kFwdRows = 128;    // query rows per forward workgroup (4 waves x 
 constexpr int kBwdRows = 128;    // query rows per dQ workgroup (4 waves x 32)
 constexpr int kTargetWGs = 256;  // one workgroup per CU on MI355X (256 CUs)
 constexpr int kMaxChunks = 64;   // cap on internal sub-splits per split
+constexpr int kStages = 4;       // LDS ring depth of K/V blocks in the key loops
 
 // Source of keys for one launch: the paged prompt pool (via the page table) or
 // the contiguous response K/V (causal).
