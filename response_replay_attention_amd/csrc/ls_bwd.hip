@@ -20,12 +20,58 @@
 
 namespace ls {
 
+// dS^T of one block as two bf16 B operands: x = raw scores (masked ones
+// -inf), dp = dP^T, lse2 = LSE*log2(e), dval = D of this lane's query.
+__device__ __forceinline__ void block_ds(const float (&x)[16], const f32x16& dp, float s2,
+                                         float lse2, float dval, bf16x8 (&dsb)[2]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], s2, -lse2));
+    dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - dval));
+  }
+}
+
+// S^T = K Q^T and dP^T = V dO^T for the block in tiles kt, vt.
+template <int D>
+__device__ __forceinline__ void block_sdp(const Lanes32<D>& tl, const uint16_t* kt,
+                                          const uint16_t* vt, const bf16x8 (&qr)[D / 16],
+                                          const bf16x8 (&dor)[D / 16], f32x16& s, f32x16& dp) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s[r] = 0.f;
+    dp[r] = 0.f;
+  }
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    s = mfma32(tl.row8(kt, kk), qr[kk], s);
+    dp = mfma32(tl.row8(vt, kk), dor[kk], dp);
+  }
+}
+
+// dQ^T[d][query] += sum_key K[key][d] dS^T[key][query] for the block in kt.
+template <int D>
+__device__ __forceinline__ void block_dq(f32x16 (&acc)[D / 32], const Lanes32<D>& tl,
+                                         const uint16_t* kt, const bf16x8 (&dsb)[2]) {
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma32(tl.col8(kt, ks, mt), dsb[ks], acc[mt]);
+  }
+}
+
 template <int D, bool RESP>
 __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
   constexpr int NKK = D / 16;
   constexpr int NMT = D / 32;
   constexpr int TILE = kBN * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // [buf][K,V]
+  constexpr int NST = kStages;
+  constexpr int NIW = BlockLoader<D>::NIW;  // copy instructions per wave per tile
+  static_assert(NST == 4, "the ring has four stages");
+  // one array per ring stage (distinct LDS objects; see the forward kernel)
+  __shared__ __attribute__((aligned(1024))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
+  uint16_t* const kst[NST] = {k0, k1, k2, k3};
+  uint16_t* const vst[NST] = {v0, v1, v2, v3};
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, lq = lane & 31;
@@ -46,6 +92,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
 
   const KeyWalk<D, RESP> walk(a, kv, unit, m0, kBwdRows);
   const int nblocks = walk.nblocks;
+  const int nfull = walk.nfull;
   const int slot = a.slot_base + unit;
 
   // Q and dO as B operands (column = query m, k = 16*kk + 8*hf + e)
@@ -70,64 +117,89 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
   const Lanes32<D> tl(hf, lq);
-  auto issue = [&](int b, int buf, int& nvalid, int& key0) {
-    walk.issue(b, smem + buf * 2 * TILE, smem + buf * 2 * TILE + TILE, wave, lane, nvalid, key0);
-  };
-  int cur_nv = 0, cur_k0 = 0;
-  if (nblocks > 0) issue(0, 0, cur_nv, cur_k0);
-  wait_async_loads();
-  __syncthreads();
+  const BlockLoader<D> ldr(wave, lane);
 
-  auto step = [&](int b, auto buf_tag) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    int nx_nv = 0, nx_k0 = 0;
-    // the other buffer was last read in block b-1, before the barrier that ended it
-    if (b + 1 < nblocks) issue(b + 1, BUF ^ 1, nx_nv, nx_k0);
+  // ---- pipelined loop over the full (unmasked) blocks.  Step b waits for
+  // K(b+1) and V(b+1), starts K(b+3) and V(b+4), computes S(b+1) and dP(b+1)
+  // while turning S(b), dP(b) into dS(b), then accumulates K(b)^T dS(b).  K(b)
+  // stays resident for two steps (scores, then dQ), so K runs three blocks
+  // ahead and V four.  Every step issues the same number of copies (blocks
+  // past the range re-read block 0), so each wait is a fixed vmcnt.
+  if (nfull > 0) {
+    wait_loads_le<0>();  // Q, dO, LSE, D have landed (the copies are invisible to the compiler)
+    size_t koff[NST];      // source offset of block j, kept from V(j)'s copy to K(j)'s
+#define LS_ISSUE_V(j, st)                                    \
+  do {                                                       \
+    koff[st] = (j) < nfull ? walk.offset(j) : 0;             \
+    load_block(ldr, vst[st], a.v + koff[st], kBN);           \
+  } while (0)
+#define LS_ISSUE_K(st) load_block(ldr, kst[st], a.k + koff[st], kBN)
+    LS_ISSUE_V(0, 0);
+    LS_ISSUE_K(0);
+    LS_ISSUE_V(1, 1);
+    LS_ISSUE_K(1);
+    LS_ISSUE_V(2, 2);
+    LS_ISSUE_K(2);
+    LS_ISSUE_V(3, 3);
+    ring_barrier<5 * NIW>();  // V(0), K(0) landed
+    f32x16 s_cur, dp_cur;
+    block_sdp<D>(tl, kst[0], vst[0], qr, dor, s_cur, dp_cur);
+#define LS_BWD_STEP(ST)                                                                \
+  if (b + (ST) < nfull) {                                                              \
+    /* K(b+1), V(b+1) landed; K stage ST-1 and V stage ST are free */                  \
+    ring_barrier<3 * NIW>();                                                           \
+    LS_ISSUE_K(((ST) + 3) % NST);                                                      \
+    LS_ISSUE_V(b + (ST) + 4, (ST));                                                    \
+    f32x16 s_next, dp_next;                                                            \
+    block_sdp<D>(tl, kst[((ST) + 1) % NST], vst[((ST) + 1) % NST], qr, dor, s_next,    \
+                 dp_next);                                                             \
+    float x[16];                                                                       \
+    for (int r = 0; r < 16; ++r) x[r] = s_cur[r];                                      \
+    bf16x8 dsb[2];                                                                     \
+    block_ds(x, dp_cur, a.s2, lse2, dval, dsb);                                        \
+    block_dq<D>(acc, tl, kst[ST], dsb);                                                \
+    s_cur = s_next;                                                                    \
+    dp_cur = dp_next;                                                                  \
+  }
+    for (int b = 0; b < nfull; b += NST) {
+      LS_BWD_STEP(0)
+      LS_BWD_STEP(1)
+      LS_BWD_STEP(2)
+      LS_BWD_STEP(3)
+    }
+#undef LS_BWD_STEP
+#undef LS_ISSUE_K
+#undef LS_ISSUE_V
+    wait_loads_le<0>();  // drain the look-ahead copies before LDS is reused
+    __syncthreads();
+  }
 
-    if (cur_nv > 0) {
-      const uint16_t* kl = smem + BUF * 2 * TILE;
-      const uint16_t* vl = kl + TILE;
-
+  // ---- masked blocks (partial last prompt page; the causal response block)
+  for (int j = nfull; j < nblocks; ++j) {
+    int nv, key0;
+    const size_t off = walk.block(j, nv, key0);
+    if (nv > 0) {
+      load_block(ldr, k0, a.k + off, nv);
+      load_block(ldr, v0, a.v + off, nv);
+    }
+    wait_loads_le<0>();
+    __syncthreads();
+    if (nv > 0) {
       f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s = mfma32(tl.row8(kl, kk), qr[kk], s);
-        dp = mfma32(tl.row8(vl, kk), dor[kk], dp);
-      }
-
-      // dS^T = P^T (dP^T - D), rounded to bf16 as the B operand of dQ^T
-      bf16x8 dsb[2];
+      block_sdp<D>(tl, k0, v0, qr, dor, s, dp);
+      float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = crow(r, hf);
-        bool ok = key < cur_nv;
-        if (RESP) ok = ok && (cur_k0 + key <= qi);
-        const float p = ok ? __builtin_amdgcn_exp2f(s[r] * a.s2 - lse2) : 0.f;
-        dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - dval));
+        bool ok = key < nv;
+        if (RESP) ok = ok && (key0 + key <= qi);
+        x[r] = ok ? s[r] : -kInf;
       }
-
-      // dQ^T[d][query] += sum_key K[key][d] dS^T[key][query]
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma32(tl.col8(kl, ks, mt), dsb[ks], acc[mt]);
-      }
+      bf16x8 dsb[2];
+      block_ds(x, dp, a.s2, lse2, dval, dsb);
+      block_dq<D>(acc, tl, k0, dsb);
     }
-
-    cur_nv = nx_nv;
-    cur_k0 = nx_k0;
-    wait_async_loads();
-    __syncthreads();
-  };
-
-  for (int b = 0; b < nblocks; b += 2) {
-    step(b, IntC<0>{});
-    if (b + 1 < nblocks) step(b + 1, IntC<1>{});
+    __syncthreads();  // tiles are rewritten by the next block
   }
 
   if (rvalid) {
