@@ -150,19 +150,27 @@ AttnArgs base_args(const ls_attn_shape& sh, const ls_page_table& pt, const void*
   return a;
 }
 
+// Workspace layouts (each piece 256-byte aligned):
+//   forward:  phys [num_pages] int32 | (chunks > 1) o, m, l partials per unit
+//   backward: phys [num_pages] int32 | D [rows] | dQ partials [units + 1]
+size_t phys_bytes(const ls_page_table& pt) { return round_up((size_t)pt.num_pages * 4, 256); }
+
 size_t fwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt) {
   const Plan p = plan_prompt(sh, pt, kFwdRows);
-  if (p.chunks <= 1) return 0;
-  const size_t rows = (size_t)sh.num_q_heads * sh.resp_len;
-  const size_t slots = (size_t)p.units;
-  return round_up(slots * rows * sh.head_dim * 4, 256) + 2 * round_up(slots * rows * 4, 256);
+  size_t n = phys_bytes(pt);
+  if (p.chunks > 1) {
+    const size_t rows = (size_t)sh.num_q_heads * sh.resp_len;
+    const size_t slots = (size_t)p.units;
+    n += round_up(slots * rows * sh.head_dim * 4, 256) + 2 * round_up(slots * rows * 4, 256);
+  }
+  return n;
 }
 
 size_t bwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt) {
   const Plan p = plan_prompt(sh, pt, kBwdRows);
   const size_t rows = (size_t)sh.num_q_heads * sh.resp_len;
   const size_t slots = (size_t)p.units + 1;
-  return round_up(rows * 4, 256) + round_up(slots * rows * sh.head_dim * 4, 256);
+  return phys_bytes(pt) + round_up(rows * 4, 256) + round_up(slots * rows * sh.head_dim * 4, 256);
 }
 
 }  // namespace
@@ -256,6 +264,7 @@ ls_status ls_replay_attn_fwd(const ls_attn_shape* sh, const ls_page_table* pt, c
     if (p && !aligned16(p)) return LS_ERR_INVALID_ARG;
   const size_t need = fwd_ws_bytes(*sh, *pt);
   if (need > 0 && (!ws || ws_bytes < need)) return LS_ERR_WORKSPACE;
+  if (need == 0) ws = nullptr;
 
   const Plan plan = plan_prompt(*sh, *pt, kFwdRows);
   const size_t rows = (size_t)sh->num_q_heads * sh->resp_len;
@@ -265,9 +274,19 @@ ls_status ls_replay_attn_fwd(const ls_attn_shape* sh, const ls_page_table* pt, c
   a.chunk_pages = plan.chunk_pages;
   a.mtiles = plan.mtiles;
 
+  char* w = static_cast<char*>(ws);
+  int32_t* phys = reinterpret_cast<int32_t*>(w);
+  w += phys_bytes(*pt);
+  a.phys = phys;
+  if (pt->num_pages > 0) {
+    st = run("resolve_pages", stream, [&] {
+      return launch_resolve_pages(pt->num_pages, pt->num_phys_pages, pt->order, pt->l2p, phys,
+                                  stream);
+    });
+    if (st != LS_OK) return st;
+  }
   float *wo = part_o, *wm = part_m, *wl = part_l;
   if (plan.chunks > 1) {
-    char* w = static_cast<char*>(ws);
     wo = reinterpret_cast<float*>(w);
     w += round_up((size_t)plan.units * rows * d * 4, 256);
     wm = reinterpret_cast<float*>(w);
@@ -339,6 +358,8 @@ ls_status ls_replay_attn_bwd(const ls_attn_shape* sh, const ls_page_table* pt, c
   const size_t rows = (size_t)sh->num_q_heads * sh->resp_len;
   const int d = sh->head_dim;
   char* w = static_cast<char*>(ws);
+  int32_t* phys = reinterpret_cast<int32_t*>(w);
+  w += phys_bytes(*pt);
   float* dvals = reinterpret_cast<float*>(w);
   float* slots = reinterpret_cast<float*>(w + round_up(rows * 4, 256));
 
@@ -352,7 +373,15 @@ ls_status ls_replay_attn_bwd(const ls_attn_shape* sh, const ls_page_table* pt, c
   a.dq_slots = slots;
   a.dk = dk_resp;
   a.dv = dv_resp;
+  a.phys = phys;
 
+  if (pt->num_pages > 0) {
+    st = run("resolve_pages", stream, [&] {
+      return launch_resolve_pages(pt->num_pages, pt->num_phys_pages, pt->order, pt->l2p, phys,
+                                  stream);
+    });
+    if (st != LS_OK) return st;
+  }
   st = run("bwd_dot", stream, [&] {
     return launch_bwd_dot((int64_t)rows, d, a.d_o, static_cast<const uint16_t*>(o), dvals, stream);
   });

@@ -127,10 +127,15 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
   // past the range re-read block 0), so each wait is a fixed vmcnt.
   if (nfull > 0) {
     wait_loads_le<0>();  // Q, dO, LSE, D have landed (the copies are invisible to the compiler)
+    // All V copies of one loop iteration (blocks b+4 .. b+7) fall in one page,
+    // whose pool offset is looked up one iteration ahead.
+    constexpr size_t kBlk = (size_t)kBN * D;
+    int ph_next = walk.page_id(0);          // page of the blocks the next iteration copies
+    size_t pcur = walk.page_base(ph_next);  // offset of the page this iteration copies from
     size_t koff[NST];      // source offset of block j, kept from V(j)'s copy to K(j)'s
 #define LS_ISSUE_V(j, st)                                    \
   do {                                                       \
-    koff[st] = (j) < nfull ? walk.offset(j) : 0;             \
+    koff[st] = (j) < nfull ? pcur + ((j) & 7) * kBlk : 0;    \
     load_block(ldr, vst[st], a.v + koff[st], kBN);           \
   } while (0)
 #define LS_ISSUE_K(st) load_block(ldr, kst[st], a.k + koff[st], kBN)
@@ -162,6 +167,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
     dp_cur = dp_next;                                                                  \
   }
     for (int b = 0; b < nfull; b += NST) {
+      pcur = walk.page_base(ph_next);
+      ph_next = b + 8 < nfull ? walk.page_id((b + 8) >> 3) : -1;
       LS_BWD_STEP(0)
       LS_BWD_STEP(1)
       LS_BWD_STEP(2)

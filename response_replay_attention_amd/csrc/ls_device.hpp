@@ -302,15 +302,13 @@ struct KeyWalk {
         nfull = nblocks - kPage / kBN;
     }
   }
-  // element offset of an unmasked prompt block's first row in the pool
-  __device__ __forceinline__ size_t offset(int b) const {
-    const int lp = ld_table(a.order, p0 + b / (kPage / kBN));
-    const int tok = (b % (kPage / kBN)) * kBN;
-    if (lp >= 0 && lp < a.num_pages) {
-      const int ph = ld_table(a.l2p, lp);
-      if (ph >= 0 && ph < a.num_phys) return (((size_t)ph * a.hkv + kv) * kPage + tok) * D;
-    }
-    return 0;
+  // Pool offset of a page of this chunk, in two halves so that the load can
+  // be issued well before the offset is needed: page_id(pg) reads the page's
+  // physical slot (one scalar load), page_base(ph) turns it into the element
+  // offset of the page's first row (0 for a slot out of range).
+  __device__ __forceinline__ int page_id(int pg) const { return ld_table(a.phys, p0 + pg); }
+  __device__ __forceinline__ size_t page_base(int ph) const {
+    return (ph >= 0 && ph < a.num_phys) ? ((size_t)ph * a.hkv + kv) * kPage * D : 0;
   }
   // any block: element offset of its first row (pool or response tensors),
   // number of valid keys (0 = skip) and, for the response, its first key index
@@ -453,8 +451,13 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * q + (x < r ? x : r) + s;
 }
 
+// max of x over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the two
+// half-waves in registers (no LDS traffic); for lane l < 32 the partner value
+// comes back in the second result, for l >= 32 in the first.
 __device__ __forceinline__ float wave_max_halves(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 }  // namespace ls

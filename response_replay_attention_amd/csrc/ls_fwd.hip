@@ -81,6 +81,76 @@ __device__ __forceinline__ void block_pv(f32x16 (&acc)[D / 32], const Lanes32<D>
   }
 }
 
+// One pipelined step: S(b+1) = K(b+1) Q^T and O^T += V(b)^T P(b), with the
+// softmax of S(b) on the VALU and the copies of two blocks three ahead.
+//
+// A single wave per SIMD pulls LDS operands at a bounded rate, so a step moves
+// as fast as its LDS read stream and the MFMAs only keep up if that stream
+// never stops.  The step is therefore cut into fixed micro-segments
+// (sched_barrier 0 between them): each issues one MFMA, the LDS read its
+// MFMA PF segments later needs, and its share of the other work -- one
+// softmax element per score MFMA, one copy instruction every second PV MFMA
+// (copies issued in a burst stall the wave behind the address unit).
+//
+// The exp2 shift mu is fixed for the whole key range, so the softmax needs no
+// per-block maximum: the lane's running maximum of raw scores (mlane) is only
+// checked against the shift once the range is done.
+template <int D>
+__device__ __forceinline__ void fwd_step(const Lanes32<D>& tl, const BlockLoader<D>& ldr,
+                                         const uint16_t* kt, const uint16_t* vt,
+                                         const bf16x8 (&qr)[D / 16], f32x16& s_cur,
+                                         f32x16 (&acc)[D / 32], float s2, float mu,
+                                         float& mlane, float& lsum, uint32_t kdst,
+                                         i32x4 kdesc, uint32_t vdst, i32x4 vdesc) {
+  constexpr int NS = D / 16;   // score MFMAs per step = PV MFMAs per step
+  constexpr int NMT = D / 32;  // 32-wide d tiles of O^T
+  constexpr int PF = 4;        // LDS prefetch distance, in MFMAs
+  constexpr int NIW = BlockLoader<D>::NIW;
+  static_assert(2 * NIW * 2 == NS, "one copy instruction every second PV MFMA");
+  bf16x8 kf[NS], vf[NS];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) kf[i] = tl.row8(kt, i);
+  f32x16 s_next;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
+  bf16x8 pb[2];
+  float mx = mlane, ls = 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    s_next = mfma32(kf[i], qr[i], s_next);
+    if (i + PF < NS) {
+      kf[i + PF] = tl.row8(kt, i + PF);
+    } else {
+      const int j = i + PF - NS;
+      vf[j] = tl.col8(vt, j / NMT, j % NMT);
+    }
+#pragma unroll
+    for (int r = i * 16 / NS; r < (i + 1) * 16 / NS; ++r) {
+      const float x = s_cur[r];
+      mx = fmaxf(mx, x);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, s2, -mu));
+      ls += p;
+      pb[r >> 3][r & 7] = to_bf16(p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    acc[j % NMT] = mfma32(vf[j], pb[j / NMT], acc[j % NMT]);
+    if (j + PF < NS) vf[j + PF] = tl.col8(vt, (j + PF) / NMT, (j + PF) % NMT);
+    if ((j & 1) == 0) {
+      const int c = j >> 1;
+      if (c < NIW) copy16_to_lds(kdst + ldr.lds0 + c * 1024, ldr.voff[c], kdesc);
+      else copy16_to_lds(vdst + ldr.lds0 + (c - NIW) * 1024, ldr.voff[c - NIW], vdesc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  mlane = mx;
+  lsum += ls;
+  s_cur = s_next;
+}
+
 template <int D, bool RESP>
 __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
   constexpr int NMT = D / 32;
@@ -148,11 +218,17 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
     // "at most two iterations' loads in flight" is a fixed vmcnt.
     if (nfull > 0) {
       wait_loads_le<0>();  // Q has landed (the copies below are invisible to the compiler)
+      // All K copies of one loop iteration (blocks b+4 .. b+7) fall in one page,
+      // whose pool offset is looked up one iteration ahead.
+      constexpr size_t kBlk = (size_t)kBN * D;
+      constexpr unsigned kBlkBytes = kBN * D * 2;
+      int ph_next = walk.page_id(0);          // page of the blocks the next iteration copies
+      size_t pcur = walk.page_base(ph_next);  // offset of the page this iteration copies from
       size_t koff[NST];  // source offset (elements) of the block held by each K stage
 #define LS_ISSUE_K(j, st)                                          \
   do {                                                             \
-    koff[st] = (j) < nfull ? walk.offset(j) : 0;                   \
-    load_block(ldr, kst[st], a.k + koff[st], kBN);       \
+    koff[st] = (j) < nfull ? pcur + ((j) & 7) * kBlk : 0;          \
+    load_block(ldr, kst[st], a.k + koff[st], kBN);                 \
   } while (0)
 #define LS_ISSUE_V(st) load_block(ldr, vst[st], a.v + koff[st], kBN)
       LS_ISSUE_K(0, 0);
@@ -164,21 +240,28 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
       LS_ISSUE_V(2);  // V(j) always goes to stage j % NST, after K(j)
       ring_barrier<3 * NLD>();  // K(0) landed
       f32x16 s_cur = block_scores<D>(tl, kst[0], qr);
-#define LS_FWD_STEP(ST)                                                               \
-  if (b + (ST) < nfull) {                                                             \
-    /* K(b+1), V(b) landed; stages ST (K) and ST-1 (V) are free */                  \
-    ring_barrier<2 * NLD>();                                                          \
-    LS_ISSUE_V(((ST) + NST - 1) % NST);                                               \
-    LS_ISSUE_K(b + (ST) + NST, (ST));                                                 \
-    const f32x16 s_next = block_scores<D>(tl, kst[((ST) + 1) % NST], qr);      \
-    float x[16];                                                                      \
-    for (int r = 0; r < 16; ++r) x[r] = s_cur[r];                                     \
-    bf16x8 pb[2];                                                                     \
-    block_probs(x, a.s2, pass0, mref, mtrue, lsum, unsafe, pb);                       \
-    block_pv<D>(acc, tl, vst[ST], pb);                                                      \
-    s_cur = s_next;                                                                   \
+      // the first block fixes the shift of pass 0
+      if (pass0 && mref == -kInf) {
+        float mx = s_cur[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+        mref = wave_max_halves(mx) * a.s2;
+      }
+      float mlane = -kInf;  // running max of this lane's raw scores in the loop
+#define LS_FWD_STEP(ST)                                                                 \
+  if (b + (ST) < nfull) {                                                               \
+    /* K(b+1), V(b) landed; stages ST (K) and ST-1 (V) are free */                    \
+    ring_barrier<2 * NLD>();                                                            \
+    constexpr int SV = ((ST) + NST - 1) % NST; /* V(b+3) goes where V(b-1) was */       \
+    const int jk = b + (ST) + NST;             /* K(b+4) goes where K(b) was */         \
+    koff[ST] = jk < nfull ? pcur + (jk & 7) * kBlk : 0;                                 \
+    fwd_step<D>(tl, ldr, kst[((ST) + 1) % NST], vst[ST], qr, s_cur, acc, a.s2, mref,    \
+                mlane, lsum, lds_addr(kst[ST]), block_desc(a.k + koff[ST], kBlkBytes),  \
+                lds_addr(vst[SV]), block_desc(a.v + koff[SV], kBlkBytes));              \
   }
       for (int b = 0; b < nfull; b += NST) {
+        pcur = walk.page_base(ph_next);
+        ph_next = b + 8 < nfull ? walk.page_id((b + 8) >> 3) : -1;
         LS_FWD_STEP(0)
         LS_FWD_STEP(1)
         LS_FWD_STEP(2)
@@ -187,6 +270,9 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
 #undef LS_FWD_STEP
 #undef LS_ISSUE_V
 #undef LS_ISSUE_K
+      const float mb = wave_max_halves(mlane) * a.s2;
+      mtrue = fmaxf(mtrue, mb);
+      if (pass0) unsafe = unsafe || (mb > mref + kShiftSlack);
       wait_loads_le<0>();  // drain the look-ahead loads before LDS is reused
       __syncthreads();
     }

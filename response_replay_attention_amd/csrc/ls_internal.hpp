@@ -26,6 +26,7 @@ struct AttnArgs {
   const int32_t* l2p;     // device page map (paged only)
   const int32_t* order;   // device split-major page list (paged only)
   const int32_t* offs;    // device split offsets (paged only)
+  const int32_t* phys;    // device physical slot of each page of `order` (-1: bad id)
   int64_t prompt_len;
   int32_t num_pages, num_phys, chunks, chunk_pages;
   int32_t hq, hkv, R, mtiles;
@@ -57,6 +58,9 @@ hipError_t launch_merge(int groups, int nper, int64_t rows, int head_dim, const 
                         float* out_m, float* out_l, hipStream_t s);
 hipError_t launch_bwd_dot(int64_t rows, int head_dim, const uint16_t* d_o, const uint16_t* o,
                           float* dvals, hipStream_t s);
+// phys[i] = l2p[order[i]] for i < num_pages, -1 where either id is out of range.
+hipError_t launch_resolve_pages(int32_t num_pages, int32_t num_phys, const int32_t* order,
+                                const int32_t* l2p, int32_t* phys, hipStream_t s);
 hipError_t launch_dq_reduce(int nslots, int64_t elems, const float* slots, float* dq,
                             hipStream_t s);
 

@@ -107,6 +107,32 @@ __global__ void __launch_bounds__(256) k_dq_reduce(int nslots, int64_t n4,
   }
 }
 
+// Physical slot of every page of the split-major list, resolved once per call
+// so that the key loops read one table entry per page instead of a dependent
+// pair of lookups.
+__global__ void __launch_bounds__(256) k_resolve_pages(int32_t num_pages, int32_t num_phys,
+                                                       const int32_t* __restrict__ order,
+                                                       const int32_t* __restrict__ l2p,
+                                                       int32_t* __restrict__ phys) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= num_pages) return;
+  const int lp = order[i];
+  int ph = -1;
+  if (lp >= 0 && lp < num_pages) {
+    const int t = l2p[lp];
+    if (t >= 0 && t < num_phys) ph = t;
+  }
+  phys[i] = ph;
+}
+
+hipError_t launch_resolve_pages(int32_t num_pages, int32_t num_phys, const int32_t* order,
+                                const int32_t* l2p, int32_t* phys, hipStream_t s) {
+  if (num_pages <= 0) return hipSuccess;
+  dim3 g((unsigned)((num_pages + 255) / 256)), b(256);
+  hipLaunchKernelGGL(k_resolve_pages, g, b, 0, s, num_pages, num_phys, order, l2p, phys);
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(int groups, int nper, int64_t rows, int head_dim, const float* po,
                         const float* pm, const float* pl, bool final, void* out_o, float* out_m,
                         float* out_l, hipStream_t s) {
