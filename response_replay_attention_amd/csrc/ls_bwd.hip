@@ -59,6 +59,72 @@ __device__ __forceinline__ void block_dq(f32x16 (&acc)[D / 32], const Lanes32<D>
   }
 }
 
+// One pipelined step of the prompt dQ loop: S(b+1) = K(b+1) Q^T and
+// dP(b+1) = V(b+1) dO^T, dS(b) on the VALU, then dQ^T += K(b)^T dS(b)^T, and
+// the copies of K(b+3) and V(b+4).  As in the forward, the step is a fixed
+// sequence of sched_barrier-fenced micro-segments that keeps the wave's LDS
+// read stream continuous: one MFMA each, the operand read PF MFMAs ahead, one
+// dS element every second score segment, one copy every second dQ segment.
+template <int D>
+__device__ __forceinline__ void bwd_step(const Lanes32<D>& tl, const BlockLoader<D>& ldr,
+                                         const uint16_t* kn, const uint16_t* vn,
+                                         const uint16_t* kc, const bf16x8 (&qr)[D / 16],
+                                         const bf16x8 (&dor)[D / 16], f32x16& s_cur,
+                                         f32x16& dp_cur, f32x16 (&acc)[D / 32], float s2,
+                                         float lse2, float dval, uint32_t kdst, i32x4 kdesc,
+                                         uint32_t vdst, i32x4 vdesc) {
+  constexpr int NS = D / 16;   // k-steps of the score products = dQ MFMAs per step
+  constexpr int NA = 2 * NS;   // score + dP MFMAs per step
+  constexpr int NMT = D / 32;
+  constexpr int PF = 4;        // LDS prefetch distance, in MFMAs
+  constexpr int NIW = BlockLoader<D>::NIW;
+  static_assert(2 * NIW * 2 == NS, "one copy instruction every second dQ MFMA");
+  bf16x8 rf[NA], cf[NS];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) rf[i] = (i & 1) ? tl.row8(vn, i >> 1) : tl.row8(kn, i >> 1);
+  f32x16 s_next, dp_next;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s_next[r] = 0.f;
+    dp_next[r] = 0.f;
+  }
+  bf16x8 dsb[2];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    if (i & 1) dp_next = mfma32(rf[i], dor[i >> 1], dp_next);
+    else s_next = mfma32(rf[i], qr[i >> 1], s_next);
+    if (i + PF < NA) {
+      const int n = i + PF;
+      rf[n] = (n & 1) ? tl.row8(vn, n >> 1) : tl.row8(kn, n >> 1);
+    } else {
+      const int j = i + PF - NA;
+      cf[j] = tl.col8(kc, j / NMT, j % NMT);
+    }
+    if (i & 1) {
+#pragma unroll
+      for (int r = (i >> 1) * 16 / NS; r < ((i >> 1) + 1) * 16 / NS; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], s2, -lse2));
+        dsb[r >> 3][r & 7] = to_bf16(p * (dp_cur[r] - dval));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    acc[j % NMT] = mfma32(cf[j], dsb[j / NMT], acc[j % NMT]);
+    if (j + PF < NS) cf[j + PF] = tl.col8(kc, (j + PF) / NMT, (j + PF) % NMT);
+    if ((j & 1) == 0) {
+      const int c = j >> 1;
+      if (c < NIW) copy16_to_lds(kdst + ldr.lds0 + c * 1024, ldr.voff[c], kdesc);
+      else copy16_to_lds(vdst + ldr.lds0 + (c - NIW) * 1024, ldr.voff[c - NIW], vdesc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  s_cur = s_next;
+  dp_cur = dp_next;
+}
+
 template <int D, bool RESP>
 __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
   constexpr int NKK = D / 16;
@@ -130,6 +196,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
     // All V copies of one loop iteration (blocks b+4 .. b+7) fall in one page,
     // whose pool offset is looked up one iteration ahead.
     constexpr size_t kBlk = (size_t)kBN * D;
+    constexpr unsigned kBlkBytes = kBN * D * 2;
     int ph_next = walk.page_id(0);          // page of the blocks the next iteration copies
     size_t pcur = walk.page_base(ph_next);  // offset of the page this iteration copies from
     size_t koff[NST];      // source offset of block j, kept from V(j)'s copy to K(j)'s
@@ -149,22 +216,17 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
     ring_barrier<5 * NIW>();  // V(0), K(0) landed
     f32x16 s_cur, dp_cur;
     block_sdp<D>(tl, kst[0], vst[0], qr, dor, s_cur, dp_cur);
-#define LS_BWD_STEP(ST)                                                                \
-  if (b + (ST) < nfull) {                                                              \
-    /* K(b+1), V(b+1) landed; K stage ST-1 and V stage ST are free */                  \
-    ring_barrier<3 * NIW>();                                                           \
-    LS_ISSUE_K(((ST) + 3) % NST);                                                      \
-    LS_ISSUE_V(b + (ST) + 4, (ST));                                                    \
-    f32x16 s_next, dp_next;                                                            \
-    block_sdp<D>(tl, kst[((ST) + 1) % NST], vst[((ST) + 1) % NST], qr, dor, s_next,    \
-                 dp_next);                                                             \
-    float x[16];                                                                       \
-    for (int r = 0; r < 16; ++r) x[r] = s_cur[r];                                      \
-    bf16x8 dsb[2];                                                                     \
-    block_ds(x, dp_cur, a.s2, lse2, dval, dsb);                                        \
-    block_dq<D>(acc, tl, kst[ST], dsb);                                                \
-    s_cur = s_next;                                                                    \
-    dp_cur = dp_next;                                                                  \
+#define LS_BWD_STEP(ST)                                                                  \
+  if (b + (ST) < nfull) {                                                                \
+    /* K(b+1), V(b+1) landed; K stage ST-1 and V stage ST are free */                   \
+    ring_barrier<3 * NIW>();                                                             \
+    constexpr int SK = ((ST) + 3) % NST; /* K(b+3) goes where K(b-1) was */              \
+    const int jv = b + (ST) + 4;         /* V(b+4) goes where V(b) was */                \
+    koff[ST] = jv < nfull ? pcur + (jv & 7) * kBlk : 0;                                  \
+    bwd_step<D>(tl, ldr, kst[((ST) + 1) % NST], vst[((ST) + 1) % NST], kst[ST], qr, dor,  \
+                s_cur, dp_cur, acc, a.s2, lse2, dval, lds_addr(kst[SK]),                 \
+                block_desc(a.k + koff[SK], kBlkBytes), lds_addr(vst[ST]),                \
+                block_desc(a.v + koff[ST], kBlkBytes));                                  \
   }
     for (int b = 0; b < nfull; b += NST) {
       pcur = walk.page_base(ph_next);
