@@ -130,6 +130,44 @@ struct Lanes32 {
   }
 };
 
+// The same operand addresses in two registers instead of sixteen.  In every
+// address above the lane-dependent part and the swizzled chunk field occupy
+// disjoint bits, so
+//     rb[k7]     = rbx ^ (16*k7)            rbx = lq*D | 8*(hf ^ swf(lq))
+//     tb[c][m3]  = tbx ^ (16*c + 32*m3)     tbx = (4*hf + e)*D | 4*(L & 1)
+//                                                 | 8*(b0 | 2*g1 | 4*e)
+// and each read costs one v_xor.  refresh() hides the two bases from
+// loop-invariant code motion, which would otherwise precompute all sixteen
+// addresses again.  Used where the register budget is 256 per wave.
+template <int D>
+struct LanesX {
+  int rbx, tbx;
+  __device__ __forceinline__ LanesX(int hf, int lq) {
+    rbx = (lq * D) | (8 * (hf ^ swf(lq)));
+    const int L = lq & 15, g1 = (lq >> 4) & 1, e = L >> 2;
+    const int b0 = ((L >> 1) & 1) ^ hf;
+    tbx = ((4 * hf + e) * D) | (4 * (L & 1)) | (8 * (b0 | 2 * g1 | 4 * e));
+  }
+  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(rbx), "+v"(tbx)); }
+  __device__ __forceinline__ bf16x8 row8(const uint16_t* tile, int kk) const {
+    return ld_bf16x8(tile + (rbx ^ (16 * (kk & 7))) + 128 * (kk >> 3));
+  }
+  __device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int ks, int mt) const {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint16_t* base = tile + 16 * ks * D + 128 * (mt >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + (tbx ^ (32 * (mt & 3)))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + 8 * D + (tbx ^ (16 + 32 * (mt & 3)))));
+    const s16x4 v[2] = {lo, hi};
+    u16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = (unsigned short)v[t >> 2][t & 3];
+    return __builtin_bit_cast(bf16x8, r);
+  }
+};
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Asynchronous copies of [32][D] bf16 blocks (row stride D) into LDS tiles,

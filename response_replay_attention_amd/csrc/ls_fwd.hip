@@ -32,7 +32,7 @@ namespace ls {
 
 // S^T[key][query] = sum_d K[key][d] Q[query][d] for the block in tile kt.
 template <int D>
-__device__ __forceinline__ f32x16 block_scores(const Lanes32<D>& tl, const uint16_t* kt,
+__device__ __forceinline__ f32x16 block_scores(const LanesX<D>& tl, const uint16_t* kt,
                                                const bf16x8 (&qr)[D / 16]) {
   f32x16 s;
 #pragma unroll
@@ -72,7 +72,7 @@ __device__ __forceinline__ void block_probs(const float (&x)[16], float s2, bool
 
 // O^T[d][query] += sum_key V[key][d] P^T[key][query] for the block in tile vt.
 template <int D>
-__device__ __forceinline__ void block_pv(f32x16 (&acc)[D / 32], const Lanes32<D>& tl,
+__device__ __forceinline__ void block_pv(f32x16 (&acc)[D / 32], const LanesX<D>& tl,
                                          const uint16_t* vt, const bf16x8 (&pb)[2]) {
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) {
@@ -81,66 +81,85 @@ __device__ __forceinline__ void block_pv(f32x16 (&acc)[D / 32], const Lanes32<D>
   }
 }
 
-// One pipelined step: S(b+1) = K(b+1) Q^T and O^T += V(b)^T P(b), with the
-// softmax of S(b) on the VALU and the copies of two blocks three ahead.
+// One step over a full key block b: S(b) = K(b) Q^T, P(b) = exp2(S s log2e -
+// mu) on the VALU, O^T += V(b)^T P(b), and the copies of block b+3.  Two
+// waves share each SIMD, so the hardware interleaves one wave's LDS waits
+// with the other's MFMAs; inside a wave the step is still a fixed sequence of
+// sched_barrier-fenced micro-segments (one MFMA, the LDS read its MFMA PF
+// segments later needs, one copy instruction every CEV PV MFMAs), which keeps
+// the wave's LDS read stream steady.
 //
-// A single wave per SIMD pulls LDS operands at a bounded rate, so a step moves
-// as fast as its LDS read stream and the MFMAs only keep up if that stream
-// never stops.  The step is therefore cut into fixed micro-segments
-// (sched_barrier 0 between them): each issues one MFMA, the LDS read its
-// MFMA PF segments later needs, and its share of the other work -- one
-// softmax element per score MFMA, one copy instruction every second PV MFMA
-// (copies issued in a burst stall the wave behind the address unit).
-//
-// The exp2 shift mu is fixed for the whole key range, so the softmax needs no
-// per-block maximum: the lane's running maximum of raw scores (mlane) is only
-// checked against the shift once the range is done.
-template <int D>
-__device__ __forceinline__ void fwd_step(const Lanes32<D>& tl, const BlockLoader<D>& ldr,
+// The exp2 shift mu is fixed for the whole key range (set from the first
+// block's max when `first`), so the softmax needs no per-block maximum: the
+// lane's running maximum of raw scores (mlane) is checked against the shift
+// once the range is done.
+// MASK: keys at index >= nvalid, and (response block) keys after the query's
+// own position qi, are masked; COPY: issue the block copies.
+template <int D, bool MASK, bool COPY>
+__device__ __forceinline__ void fwd_step(const LanesX<D>& tl, const BlockLoader<D, kFwdWaves>& ldr,
                                          const uint16_t* kt, const uint16_t* vt,
-                                         const bf16x8 (&qr)[D / 16], f32x16& s_cur,
-                                         f32x16 (&acc)[D / 32], float s2, float mu,
-                                         float& mlane, float& lsum, uint32_t kdst,
-                                         i32x4 kdesc, uint32_t vdst, i32x4 vdesc) {
+                                         const bf16x8 (&qr)[D / 16], f32x16 (&acc)[D / 32],
+                                         float s2, bool first, float& mu, float& mlane,
+                                         float& lsum, uint32_t kdst, i32x4 kdesc, uint32_t vdst,
+                                         i32x4 vdesc, int nvalid = kBN, int kmax = 0x7fffffff,
+                                         int hf = 0) {
   constexpr int NS = D / 16;   // score MFMAs per step = PV MFMAs per step
   constexpr int NMT = D / 32;  // 32-wide d tiles of O^T
-  constexpr int PF = 4;        // LDS prefetch distance, in MFMAs
-  constexpr int NIW = BlockLoader<D>::NIW;
-  static_assert(2 * NIW * 2 == NS, "one copy instruction every second PV MFMA");
+  constexpr int PF = 1;        // LDS prefetch distance, in MFMAs
+  constexpr int NIW = BlockLoader<D, kFwdWaves>::NIW;
+  constexpr int CEV = NS / (2 * NIW);  // PV segments per copy instruction
+  static_assert(CEV * 2 * NIW == NS, "copy instructions spread evenly over the PV MFMAs");
   bf16x8 kf[NS], vf[NS];
 #pragma unroll
   for (int i = 0; i < PF; ++i) kf[i] = tl.row8(kt, i);
-  f32x16 s_next;
+  f32x16 s;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
-  bf16x8 pb[2];
-  float mx = mlane, ls = 0.f;
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    s_next = mfma32(kf[i], qr[i], s_next);
+    s = mfma32(kf[i], qr[i], s);
     if (i + PF < NS) {
       kf[i + PF] = tl.row8(kt, i + PF);
     } else {
       const int j = i + PF - NS;
       vf[j] = tl.col8(vt, j / NMT, j % NMT);
     }
-#pragma unroll
-    for (int r = i * 16 / NS; r < (i + 1) * 16 / NS; ++r) {
-      const float x = s_cur[r];
-      mx = fmaxf(mx, x);
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, s2, -mu));
-      ls += p;
-      pb[r >> 3][r & 7] = to_bf16(p);
-    }
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (MASK) {
+    // key crow(r, hf) = 4*hf + 8*(r/4) + r%4 of the block is visible iff it is
+    // < nvalid and <= kmax; compared as compile-time row offsets against two
+    // per-lane thresholds, so no key index is kept in a register
+    const int lim = min(nvalid - 1, kmax) - 4 * hf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) <= lim) ? s[r] : -kInf;
+  }
+  if (first) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mu = wave_max_halves(mx) * s2;
+  }
+  bf16x8 pb[2];
+  float mx = mlane, ls = 0.f;
+  // a fully masked first block leaves no shift (masked blocks only)
+  const float mus = (MASK && mu == -kInf) ? 0.f : mu;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float x = s[r];
+    mx = fmaxf(mx, x);
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, s2, -mus));
+    ls += p;
+    pb[r >> 3][r & 7] = to_bf16(p);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     acc[j % NMT] = mfma32(vf[j], pb[j / NMT], acc[j % NMT]);
     if (j + PF < NS) vf[j + PF] = tl.col8(vt, (j + PF) / NMT, (j + PF) % NMT);
-    if ((j & 1) == 0) {
-      const int c = j >> 1;
+    if (COPY && j % CEV == 0) {
+      const int c = j / CEV;
       if (c < NIW) copy16_to_lds(kdst + ldr.lds0 + c * 1024, ldr.voff[c], kdesc);
       else copy16_to_lds(vdst + ldr.lds0 + (c - NIW) * 1024, ldr.voff[c - NIW], vdesc);
     }
@@ -148,15 +167,14 @@ __device__ __forceinline__ void fwd_step(const Lanes32<D>& tl, const BlockLoader
   }
   mlane = mx;
   lsum += ls;
-  s_cur = s_next;
 }
 
 template <int D, bool RESP>
-__global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
+__global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   constexpr int NMT = D / 32;
   constexpr int TILE = kBN * D;                     // elements of one K or V block
   constexpr int NST = kStages;                      // ring depth (4)
-  constexpr int NLD = 2 * BlockLoader<D>::NIW;      // load instructions per wave per block
+  constexpr int NLD = 2 * BlockLoader<D, kFwdWaves>::NIW;  // copy instructions per wave per block
   // One array per ring stage: distinct LDS objects let the compiler tell the
   // stages apart, so a read of one stage does not wait for the copies still
   // in flight into the others.
@@ -193,8 +211,8 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qr[kk] = ld_bf16x8(qp + 16 * kk);
   }
-  const Lanes32<D> tl(hf, lq);
-  const BlockLoader<D> ldr(wave, lane);
+  LanesX<D> tl(hf, lq);
+  const BlockLoader<D, kFwdWaves> ldr(wave, lane);
 
   f32x16 acc[NMT];
   float mref = -kInf;   // exp2 shift of this query (log2 units)
@@ -211,97 +229,95 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
     bool unsafe = false;
     const bool pass0 = pass == 0;
 
-    // ---- pipelined loop over the full (unmasked) blocks.  Iteration b waits
-    // for K(b+1) and V(b), starts K(b+4) and V(b+3), computes S(b+1) while
-    // turning S(b) into P(b), then accumulates V(b)^T P(b).  Every iteration
-    // issues exactly NLD loads (blocks past the range re-read block 0), so
-    // "at most two iterations' loads in flight" is a fixed vmcnt.
+    // ---- loop over the full (unmasked) blocks through the 4-stage ring.
+    // Step b waits for K(b) and V(b), computes block b and starts the copies
+    // of block b+3 into the stage block b-1 used.  Every step issues exactly
+    // NLD copies (blocks past the range re-read block 0), so "at most two
+    // steps' copies in flight" is a fixed vmcnt.
     if (nfull > 0) {
       wait_loads_le<0>();  // Q has landed (the copies below are invisible to the compiler)
-      // All K copies of one loop iteration (blocks b+4 .. b+7) fall in one page,
-      // whose pool offset is looked up one iteration ahead.
       constexpr size_t kBlk = (size_t)kBN * D;
       constexpr unsigned kBlkBytes = kBN * D * 2;
-      int ph_next = walk.page_id(0);          // page of the blocks the next iteration copies
-      size_t pcur = walk.page_base(ph_next);  // offset of the page this iteration copies from
-      size_t koff[NST];  // source offset (elements) of the block held by each K stage
-#define LS_ISSUE_K(j, st)                                          \
-  do {                                                             \
-    koff[st] = (j) < nfull ? pcur + ((j) & 7) * kBlk : 0;          \
-    load_block(ldr, kst[st], a.k + koff[st], kBN);                 \
-  } while (0)
-#define LS_ISSUE_V(st) load_block(ldr, vst[st], a.v + koff[st], kBN)
-      LS_ISSUE_K(0, 0);
-      LS_ISSUE_K(1, 1);
-      LS_ISSUE_V(0);
-      LS_ISSUE_K(2, 2);
-      LS_ISSUE_V(1);
-      LS_ISSUE_K(3, 3);
-      LS_ISSUE_V(2);  // V(j) always goes to stage j % NST, after K(j)
-      ring_barrier<3 * NLD>();  // K(0) landed
-      f32x16 s_cur = block_scores<D>(tl, kst[0], qr);
-      // the first block fixes the shift of pass 0
-      if (pass0 && mref == -kInf) {
-        float mx = s_cur[0];
+      constexpr int BPP = kPage / kBN;  // blocks per page
+      const int npg = nfull / BPP;      // full pages of this range
+      // pool offsets of page pn and pn+1, and the id of page pn+2 (loaded one
+      // page ahead of its use); copies address block j through page j / BPP
+      int pn = 0;
+      size_t base0 = walk.page_base(walk.page_id(0));
+      size_t base1 = npg > 1 ? walk.page_base(walk.page_id(1)) : 0;
+      int id2 = npg > 2 ? walk.page_id(2) : -1;
+#define LS_BLOCK_OFF(j)                                                              \
+  ((j) < nfull ? (((j) / BPP == pn) ? base0 : base1) + ((j) % BPP) * kBlk : (size_t)0)
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-        mref = wave_max_halves(mx) * a.s2;
+      for (int j = 0; j < 3; ++j) {
+        const size_t off = LS_BLOCK_OFF(j);
+        load_block(ldr, kst[j], a.k + off, kBN);
+        load_block(ldr, vst[j], a.v + off, kBN);
       }
-      float mlane = -kInf;  // running max of this lane's raw scores in the loop
-#define LS_FWD_STEP(ST)                                                                 \
-  if (b + (ST) < nfull) {                                                               \
-    /* K(b+1), V(b) landed; stages ST (K) and ST-1 (V) are free */                    \
-    ring_barrier<2 * NLD>();                                                            \
-    constexpr int SV = ((ST) + NST - 1) % NST; /* V(b+3) goes where V(b-1) was */       \
-    const int jk = b + (ST) + NST;             /* K(b+4) goes where K(b) was */         \
-    koff[ST] = jk < nfull ? pcur + (jk & 7) * kBlk : 0;                                 \
-    fwd_step<D>(tl, ldr, kst[((ST) + 1) % NST], vst[ST], qr, s_cur, acc, a.s2, mref,    \
-                mlane, lsum, lds_addr(kst[ST]), block_desc(a.k + koff[ST], kBlkBytes),  \
-                lds_addr(vst[SV]), block_desc(a.v + koff[SV], kBlkBytes));              \
+      float mlane = -kInf;  // running max of this lane's raw scores in the range
+      // Values the loop reads that may have been reloaded from scratch: make
+      // them resident here, so the loop body never waits on a pending reload
+      // (such a wait would also drain the ring's copies).
+      asm volatile("" ::"v"(mref), "v"(lsum), "v"(mtrue));
+#define LS_FWD_STEP(ST)                                                                  \
+  if (b + (ST) < nfull) {                                                                \
+    /* K(b), V(b) landed; stage (ST+3)%4 (block b-1) is free */                         \
+    ring_barrier<2 * NLD>();                                                             \
+    tl.refresh();                                                                        \
+    constexpr int SC = ((ST) + 3) % NST;                                                 \
+    const size_t off = LS_BLOCK_OFF(b + (ST) + 3);                                       \
+    /* pass 0 starts with no shift: its first block sets it */                          \
+    fwd_step<D, false, true>(tl, ldr, kst[ST], vst[ST], qr, acc, a.s2,                   \
+                pass0 && b + (ST) == 0, mref, mlane, lsum, lds_addr(kst[SC]),            \
+                block_desc(a.k + off, kBlkBytes), lds_addr(vst[SC]),                     \
+                block_desc(a.v + off, kBlkBytes));                                       \
   }
       for (int b = 0; b < nfull; b += NST) {
-        pcur = walk.page_base(ph_next);
-        ph_next = b + 8 < nfull ? walk.page_id((b + 8) >> 3) : -1;
+        // the copies of this iteration (blocks b+3 .. b+6) reach page (b+6)/BPP
+        if ((b + 6) / BPP > pn + 1 && b + 6 < nfull) {
+          ++pn;
+          base0 = base1;
+          base1 = walk.page_base(id2);
+          id2 = pn + 2 < npg ? walk.page_id(pn + 2) : -1;
+        }
         LS_FWD_STEP(0)
         LS_FWD_STEP(1)
         LS_FWD_STEP(2)
         LS_FWD_STEP(3)
       }
 #undef LS_FWD_STEP
-#undef LS_ISSUE_V
-#undef LS_ISSUE_K
+#undef LS_BLOCK_OFF
       const float mb = wave_max_halves(mlane) * a.s2;
       mtrue = fmaxf(mtrue, mb);
       if (pass0) unsafe = unsafe || (mb > mref + kShiftSlack);
-      wait_loads_le<0>();  // drain the look-ahead loads before LDS is reused
+      wait_loads_le<0>();  // drain the look-ahead copies before LDS is reused
       __syncthreads();
     }
 
     // ---- masked blocks (partial last prompt page; the causal response block)
-    for (int j = nfull; j < nblocks; ++j) {
-      int nv, key0;
-      const size_t off = walk.block(j, nv, key0);
-      if (nv > 0) {
-        load_block(ldr, k0, a.k + off, nv);
-        load_block(ldr, v0, a.v + off, nv);
-      }
-      wait_loads_le<0>();
-      __syncthreads();
-      if (nv > 0) {
-        const f32x16 s = block_scores<D>(tl, k0, qr);
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = crow(r, hf);
-          bool ok = key < nv;
-          if (RESP) ok = ok && (key0 + key <= qi);
-          x[r] = ok ? s[r] : -kInf;
+    {
+      float mlane = -kInf;
+      for (int j = nfull; j < nblocks; ++j) {
+        int nv, key0;
+        const size_t off = walk.block(j, nv, key0);
+        if (nv > 0) {
+          load_block(ldr, k0, a.k + off, nv);
+          load_block(ldr, v0, a.v + off, nv);
         }
-        bf16x8 pb[2];
-        block_probs(x, a.s2, pass0, mref, mtrue, lsum, unsafe, pb);
-        block_pv<D>(acc, tl, v0, pb);
+        wait_loads_le<0>();
+        __syncthreads();
+        if (nv > 0) {
+          tl.refresh();
+          const i32x4 none = {0, 0, 0, 0};
+          fwd_step<D, true, false>(tl, ldr, k0, v0, qr, acc, a.s2, pass0 && mref == -kInf, mref,
+                                   mlane, lsum, 0, none, 0, none, nv,
+                                   RESP ? qi - key0 : 0x7fffffff, hf);
+        }
+        __syncthreads();  // tiles are rewritten by the next block
       }
-      __syncthreads();  // tiles are rewritten by the next block
+      const float mb = wave_max_halves(mlane) * a.s2;
+      mtrue = fmaxf(mtrue, mb);
+      if (pass0) unsafe = unsafe || (mb > mref + kShiftSlack);
     }
 
     if (!pass0 || !__syncthreads_or(unsafe ? 1 : 0)) break;
@@ -335,7 +351,7 @@ __global__ void __launch_bounds__(256, 1) k_fwd(const AttnArgs a) {
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  dim3 g(grid), b(256);
+  dim3 g(grid), b(64 * kFwdWaves);
   if (head_dim == 256) {
     if (resp) hipLaunchKernelGGL((k_fwd<256, true>), g, b, 0, s, a);
     else hipLaunchKernelGGL((k_fwd<256, false>), g, b, 0, s, a);
