@@ -8,6 +8,11 @@ dK/dV, ordered dQ sum).  Inputs are resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+The default workload is the 2,097,152-position prefix with R = 1024 (one member).  Any name in
+``replay_inputs.WORKLOADS`` can be given; for the G = 8 group a step is the serial replay of all
+eight members (R = 512 ... 4096) over the shared prompt, `prompt_keys_per_s` counts prompt keys
+times members, and the line also carries each member's time from one extra, untimed pass.
+
 Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step
 (only unmasked scores counted: 4d flops per (head,row,key) forward; 6d per
 prompt key and 10d per response key backward, no prompt dK/dV work); the same
@@ -31,7 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
 DOMINANT = "bwd_prompt_dq"  # 60% of the algorithmic flops
 KERNELS = ("fwd_prompt", "fwd_combine", "fwd_resp", "lse_merge", "bwd_dot", "bwd_prompt_dq",
-           "bwd_resp_dq", "bwd_resp_dkdv", "dq_reduce")
+           "bwd_resp_dq", "bwd_resp_dkdv", "kv_reduce", "dq_reduce")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_prompt_dq_traffic_prefix2M.md")
 
 
@@ -141,22 +146,37 @@ def main() -> int:
 
     import torch
 
-    from replay_inputs import WORKLOADS, make_inputs
-    from response_replay_attention_amd import (PromptCache, ls_timing_enable, ls_timing_read,
-                                               ls_timing_reset, replay_backward, replay_forward)
+    from replay_inputs import GROUP_2M, GROUP_2M_RESP_LENS, WORKLOADS, make_inputs, make_response
+    from response_replay_attention_amd import (Member, PromptCache, ls_timing_enable,
+                                               ls_timing_read, ls_timing_reset, replay_backward,
+                                               replay_forward, replay_group)
 
     shape = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = make_inputs(shape, args.seed, device=dev)
+    group = shape.name == GROUP_2M.name
+    # the group replays G members of different lengths over one shared prompt;
+    # every other workload is one member
+    member_shapes = ([shape.with_(resp_len=r) for r in GROUP_2M_RESP_LENS] if group else [shape])
+    inp = make_inputs(member_shapes[0], args.seed, device=dev)
+    members = [Member(inp["q"], inp["k_resp"], inp["v_resp"], inp["d_o"])]
+    for i, sh in enumerate(member_shapes[1:], start=1):
+        r = make_response(sh, args.seed + i, device=dev)
+        members.append(Member(r["q"], r["k_resp"], r["v_resp"], r["d_o"]))
     torch.cuda.synchronize()
 
+    def make_cache():
+        return PromptCache(inp["k_pool"], inp["v_pool"], shape.prompt_len, inp["l2p"],
+                           shape.num_splits, shape.policy, shape.block_pages)
+
     def step():
-        cache = PromptCache(inp["k_pool"], inp["v_pool"], shape.prompt_len, inp["l2p"],
-                            shape.num_splits, shape.policy, shape.block_pages)
-        fwd = replay_forward(cache, inp["q"], inp["k_resp"], inp["v_resp"], shape.scale)
-        replay_backward(cache, inp["q"], inp["k_resp"], inp["v_resp"], fwd.o, fwd.lse,
-                        inp["d_o"], shape.scale)
+        cache = make_cache()
+        if group:
+            replay_group(cache, members, scale=shape.scale)
+            return
+        m = members[0]
+        fwd = replay_forward(cache, m.q, m.k_resp, m.v_resp, shape.scale)
+        replay_backward(cache, m.q, m.k_resp, m.v_resp, fwd.o, fwd.lse, m.d_o, shape.scale)
 
     for _ in range(args.warmup):
         step()
@@ -183,12 +203,15 @@ def main() -> int:
         if n:
             kern[k] = {"launches": n, "avg_ms": ms / n}
 
-    f = flops(shape)
-    step_flops = sum(f.values())
+    per_member = [flops(sh) for sh in member_shapes]
+    step_flops = sum(sum(f.values()) for f in per_member)
     ms_step = elapsed / args.steps * 1e3
     tflops = step_flops * args.steps / elapsed / 1e12
     dom = kern.get(DOMINANT, {"avg_ms": float("nan")})
-    achieved = f["bwd_prompt_dq"] / (dom["avg_ms"] * 1e-3) / 1e12
+    # the dominant kernel's launches all have the prompt's shape; their average
+    # flops per launch is the members' mean
+    dom_flops = sum(f["bwd_prompt_dq"] for f in per_member) / len(per_member)
+    achieved = dom_flops / (dom["avg_ms"] * 1e-3) / 1e12
     digest = source_digest()
     traffic = read_traffic(digest)
 
@@ -212,7 +235,7 @@ def main() -> int:
             "splits": shape.num_splits, "page_size": shape.page_size,
             "parallelism": "1 GPU; CP ranks emulated as page splits",
         },
-        "prompt_keys_per_s": round(shape.prompt_len * args.steps / elapsed, 1),
+        "prompt_keys_per_s": round(shape.prompt_len * len(members) * args.steps / elapsed, 1),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {
             "kernel": DOMINANT,
@@ -226,8 +249,20 @@ def main() -> int:
         },
         "kernels_avg_ms": {k: round(v["avg_ms"], 4) for k, v in kern.items()},
     }
+    if group:
+        out["config"]["members"] = len(members)
+        out["config"]["resp_lens"] = list(GROUP_2M_RESP_LENS)
+        # one more pass, outside the timed region, for the time of each member
+        cache = make_cache()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(members) + 1)]
+        ev[0].record()
+        for i, m in enumerate(members):
+            replay_group(cache, [m], scale=shape.scale)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        out["per_member_ms"] = [round(ev[i].elapsed_time(ev[i + 1]), 3) for i in range(len(members))]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, inp)
+        out["cpu_baseline"] = cpu_baseline(member_shapes[0], inp)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -153,7 +153,12 @@ AttnArgs base_args(const ls_attn_shape& sh, const ls_page_table& pt, const void*
 // Workspace layouts (each piece 256-byte aligned):
 //   forward:  phys [num_pages] int32 | (chunks > 1) o, m, l partials per unit
 //   backward: phys [num_pages] int32 | D [rows] | dQ partials [units + 1]
+//             | response dV/dK partials per query head [2][g][Hkv][R][d]
 size_t phys_bytes(const ls_page_table& pt) { return round_up((size_t)pt.num_pages * 4, 256); }
+
+size_t kv_part_bytes(const ls_attn_shape& sh) {
+  return round_up((size_t)2 * sh.num_q_heads * sh.resp_len * sh.head_dim * 4, 256);
+}
 
 size_t fwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt) {
   const Plan p = plan_prompt(sh, pt, kFwdRows);
@@ -170,7 +175,8 @@ size_t bwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt) {
   const Plan p = plan_prompt(sh, pt, kBwdRows);
   const size_t rows = (size_t)sh.num_q_heads * sh.resp_len;
   const size_t slots = (size_t)p.units + 1;
-  return phys_bytes(pt) + round_up(rows * 4, 256) + round_up(slots * rows * sh.head_dim * 4, 256);
+  return phys_bytes(pt) + round_up(rows * 4, 256) + round_up(slots * rows * sh.head_dim * 4, 256) +
+         kv_part_bytes(sh);
 }
 
 }  // namespace
@@ -362,6 +368,8 @@ ls_status ls_replay_attn_bwd(const ls_attn_shape* sh, const ls_page_table* pt, c
   w += phys_bytes(*pt);
   float* dvals = reinterpret_cast<float*>(w);
   float* slots = reinterpret_cast<float*>(w + round_up(rows * 4, 256));
+  float* kv_part = reinterpret_cast<float*>(w + round_up(rows * 4, 256) +
+                                            round_up(((size_t)plan.units + 1) * rows * d * 4, 256));
 
   AttnArgs a = base_args(*sh, *pt, q, k_pool, v_pool);
   a.chunks = plan.chunks;
@@ -373,6 +381,7 @@ ls_status ls_replay_attn_bwd(const ls_attn_shape* sh, const ls_page_table* pt, c
   a.dq_slots = slots;
   a.dk = dk_resp;
   a.dv = dv_resp;
+  a.kv_part = kv_part;
   a.phys = phys;
 
   if (pt->num_pages > 0) {
@@ -398,6 +407,12 @@ ls_status ls_replay_attn_bwd(const ls_attn_shape* sh, const ls_page_table* pt, c
   st = run("bwd_resp_dq", stream, [&] { return launch_bwd_dq(r, d, true, rgrid, stream); });
   if (st != LS_OK) return st;
   st = run("bwd_resp_dkdv", stream, [&] { return launch_bwd_dkdv(r, d, stream); });
+  if (st != LS_OK) return st;
+  st = run("kv_reduce", stream, [&] {
+    return launch_kv_reduce(sh->num_q_heads / sh->num_kv_heads,
+                            (int64_t)sh->num_kv_heads * sh->resp_len * d, kv_part, dv_resp, dk_resp,
+                            stream);
+  });
   if (st != LS_OK) return st;
   return run("dq_reduce", stream, [&] {
     return launch_dq_reduce(plan.units + 1, (int64_t)rows * d, slots, dq, stream);

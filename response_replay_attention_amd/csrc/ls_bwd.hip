@@ -289,14 +289,16 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
   }
 }
 
-// dK or dV of 32 response keys [j0, j0+32) of KV head kv, one wave per
-// workgroup, key-stationary: loops over every query head of the group and every
-// query block i0 >= j0, accumulating
+// dK or dV of 32 response keys [j0, j0+32) of KV head kv from the query head
+// kv*g + blockIdx.z, one wave per workgroup, key-stationary: loops over every
+// query block i0 >= j0 of that head, accumulating
 //   DV:  dV^T[d][key] += sum_query dO[query][d] P[query][key]
 //   DK:  dK^T[d][key] += sum_query Q[query][d]  dS[query][key]
 // with S = Q K^T and dP = dO V^T recomputed in the (query x key) orientation.
-// dV and dK are separate launches so each needs only one 128-register
-// accumulator set.
+// Each head writes its own fp32 partial (k_kv_reduce sums the g heads of a
+// group in head order), so the launch has g times more workgroups than key
+// blocks and needs no atomics.  dV and dK are separate launches so each needs
+// only one 128-register accumulator set.
 template <int D, bool DK>
 __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
   constexpr int NKK = D / 16;
@@ -307,6 +309,7 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
 
   const int lane = threadIdx.x, hf = lane >> 5, lq = lane & 31;
   const int kv = blockIdx.y;
+  const int hh = blockIdx.z;  // query head within the group
   const int j0 = blockIdx.x * kBN;
   const int g = a.hq / a.hkv;
   uint16_t* kt = smem;
@@ -329,7 +332,7 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
-  for (int hh = 0; hh < g; ++hh) {
+  {
     const int h = kv * g + hh;
     for (int i0 = j0; i0 < a.R; i0 += kBN) {
       const int nq = min(kBN, a.R - i0);
@@ -382,7 +385,7 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
 
   if (key < a.R) {
     const float mul = DK ? a.scale : 1.f;
-    float* op = (DK ? a.dk : a.dv) + ((size_t)kv * a.R + key) * D + 4 * hf;
+    float* op = a.kv_part + ((((size_t)(DK ? g : 0) + hh) * a.hkv + kv) * a.R + key) * D + 4 * hf;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
@@ -412,7 +415,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, h
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s) {
-  dim3 g((a.R + kBN - 1) / kBN, a.hkv), b(64);
+  dim3 g((a.R + kBN - 1) / kBN, a.hkv, a.hq / a.hkv), b(64);
   if (head_dim == 256) {
     hipLaunchKernelGGL((k_bwd_resp_kv<256, false>), g, b, 0, s, a);
     hipLaunchKernelGGL((k_bwd_resp_kv<256, true>), g, b, 0, s, a);

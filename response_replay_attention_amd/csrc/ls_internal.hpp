@@ -45,11 +45,15 @@ struct AttnArgs {
   float* dq_slots;        // fp32 [slots, Hq*R, d]
   float* dk;              // fp32 [Hkv, R, d]
   float* dv;
+  float* kv_part;         // fp32 [2][g][Hkv][R][d] per-query-head dV (0) / dK (1) partials
 };
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s);
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s);
+// dv = sum_h kv_part[0][h], dk = sum_h kv_part[1][h] in head order
+hipError_t launch_kv_reduce(int g, int64_t elems, const float* part, float* dv, float* dk,
+                            hipStream_t s);
 
 // Merge `nper` consecutive parts per group: group c reads parts
 // [c*nper, (c+1)*nper).  final=true writes bf16 O and natural-log LSE;

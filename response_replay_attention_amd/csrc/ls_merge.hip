@@ -133,6 +133,39 @@ hipError_t launch_resolve_pages(int32_t num_pages, int32_t num_phys, const int32
   return hipGetLastError();
 }
 
+// dv = sum over the g query heads of part[0], dk = sum of part[1], in head
+// order (deterministic); part is [2][g][elems].
+__global__ void __launch_bounds__(256) k_kv_reduce(int g, int64_t n4, const float4* __restrict__ part,
+                                                   float4* __restrict__ dv, float4* __restrict__ dk) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const float4* p = part + (size_t)w * g * n4 + i;
+      float4 acc = p[0];
+      for (int h = 1; h < g; ++h) {
+        const float4 v = p[(size_t)h * n4];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      (w == 0 ? dv : dk)[i] = acc;
+    }
+  }
+}
+
+hipError_t launch_kv_reduce(int g, int64_t elems, const float* part, float* dv, float* dk,
+                            hipStream_t s) {
+  const int64_t n4 = elems / 4;
+  if (n4 <= 0) return hipSuccess;
+  const int64_t want = (n4 + 255) / 256;
+  dim3 gr((unsigned)(want < 4096 ? want : 4096)), b(256);
+  hipLaunchKernelGGL(k_kv_reduce, gr, b, 0, s, g, n4, reinterpret_cast<const float4*>(part),
+                     reinterpret_cast<float4*>(dv), reinterpret_cast<float4*>(dk));
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(int groups, int nper, int64_t rows, int head_dim, const float* po,
                         const float* pm, const float* pl, bool final, void* out_o, float* out_m,
                         float* out_l, hipStream_t s) {
