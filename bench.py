@@ -6,12 +6,14 @@ prompt, the causal response block, the exact LSE merge, and the
 response-only backward (D = rowsum(dO*O), per-split dQ, response dQ, response
 dK/dV, ordered dQ sum).  Inputs are resident in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--score]
 
 The default workload is the 2,097,152-position prefix with R = 1024 (one member).  Any name in
 ``replay_inputs.WORKLOADS`` can be given; for the G = 8 group a step is the serial replay of all
 eight members (R = 512 ... 4096) over the shared prompt, `prompt_keys_per_s` counts prompt keys
 times members, and the line also carries each member's time from one extra, untimed pass.
+``--score`` times forward-only scoring instead: all members in one pass over the prompt
+(``ls_replay_attn_fwd_members``) and the merge, counting forward flops only.
 
 Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step
 (only unmasked scores counted: 4d flops per (head,row,key) forward; 6d per
@@ -134,6 +136,9 @@ def main() -> int:
     ap.add_argument("--workload", default="prefix_24x4_d256_p2097152_r1024_s8")
     ap.add_argument("--seed", type=int, default=20260002)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--score", action="store_true",
+                    help="forward-only scoring of all members in one pass over the prompt "
+                         "(merged O and LSE per member, no backward)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -149,7 +154,7 @@ def main() -> int:
     from replay_inputs import GROUP_2M, GROUP_2M_RESP_LENS, WORKLOADS, make_inputs, make_response
     from response_replay_attention_amd import (Member, PromptCache, ls_timing_enable,
                                                ls_timing_read, ls_timing_reset, replay_backward,
-                                               replay_forward, replay_group)
+                                               replay_forward, replay_group, score_group)
 
     shape = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -171,6 +176,9 @@ def main() -> int:
 
     def step():
         cache = make_cache()
+        if args.score:
+            score_group(cache, members, scale=shape.scale)
+            return
         if group:
             replay_group(cache, members, scale=shape.scale)
             return
@@ -204,16 +212,21 @@ def main() -> int:
             kern[k] = {"launches": n, "avg_ms": ms / n}
 
     per_member = [flops(sh) for sh in member_shapes]
+    if args.score:  # forward work only
+        per_member = [{k: v for k, v in f.items() if k.startswith("fwd")} for f in per_member]
     step_flops = sum(sum(f.values()) for f in per_member)
     ms_step = elapsed / args.steps * 1e3
     tflops = step_flops * args.steps / elapsed / 1e12
-    dom = kern.get(DOMINANT, {"avg_ms": float("nan")})
-    # the dominant kernel's launches all have the prompt's shape; their average
-    # flops per launch is the members' mean
-    dom_flops = sum(f["bwd_prompt_dq"] for f in per_member) / len(per_member)
+    dominant = "fwd_prompt" if args.score else DOMINANT
+    dom = kern.get(dominant, {"avg_ms": float("nan")})
+    # the dominant kernel's flops per launch: the members' mean (one launch per
+    # member), or all members at once when scoring
+    dom_flops = sum(f["fwd_prompt" if args.score else "bwd_prompt_dq"] for f in per_member)
+    if not args.score:
+        dom_flops /= len(per_member)
     achieved = dom_flops / (dom["avg_ms"] * 1e-3) / 1e12
     digest = source_digest()
-    traffic = read_traffic(digest)
+    traffic = None if args.score else read_traffic(digest)
 
     out = {
         "metric": "replay-attn fwd+bwd TFLOP/s & prompt-keys/s at 2M prefix; % bf16 MFMA peak",
@@ -238,7 +251,7 @@ def main() -> int:
         "prompt_keys_per_s": round(shape.prompt_len * len(members) * args.steps / elapsed, 1),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {
-            "kernel": DOMINANT,
+            "kernel": dominant,
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
@@ -249,7 +262,10 @@ def main() -> int:
         },
         "kernels_avg_ms": {k: round(v["avg_ms"], 4) for k, v in kern.items()},
     }
-    if group:
+    if args.score:
+        out["metric"] = "group scoring (forward only) TFLOP/s & prompt-keys/s; % bf16 MFMA peak"
+        out["config"]["mode"] = "score"
+    if group and not args.score:
         out["config"]["members"] = len(members)
         out["config"]["resp_lens"] = list(GROUP_2M_RESP_LENS)
         # one more pass, outside the timed region, for the time of each member
@@ -261,6 +277,9 @@ def main() -> int:
             ev[i + 1].record()
         torch.cuda.synchronize()
         out["per_member_ms"] = [round(ev[i].elapsed_time(ev[i + 1]), 3) for i in range(len(members))]
+    if group and args.score:
+        out["config"]["members"] = len(members)
+        out["config"]["resp_lens"] = list(GROUP_2M_RESP_LENS)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(member_shapes[0], inp)
     print(json.dumps(out), flush=True)

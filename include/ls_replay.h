@@ -165,6 +165,33 @@ ls_status ls_replay_attn_fwd(const ls_attn_shape* shape, const ls_page_table* pt
                              float* part_o, float* part_m, float* part_l,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ls_replay_attn_fwd_members -- the same forward for a group of G response
+ * branches of one prompt in a single pass over the prompt pages (graph-free
+ * scoring of the whole group: the pages score every member against the one
+ * captured prompt before the per-member replay; DeepRead summary page,
+ * "Method"; LongStraw review page, section 2, item 3).  Members are stacked
+ * along the response axis: member k owns response rows
+ * [member_offsets[k], member_offsets[k+1]) of every head, so q is
+ * [Hq, R, d], k_resp / v_resp are [Hkv, R, d] and the partials are laid out
+ * exactly as for ls_replay_attn_fwd with R = shape->resp_len = the total.
+ * Every prompt key is visible to every row; response key j is visible to row
+ * i only when both lie in the same member and j <= i.  Part S is the response
+ * block, parts c < S the prompt splits, as above; ls_lse_merge then gives each
+ * member's O and LSE in its rows.
+ *   num_members          G >= 1
+ *   member_offsets       host int32 [G+1]: 0 = offs[0] < offs[1] < ... < offs[G] = R
+ *   member_offsets_dev   device copy of member_offsets (may be NULL when G == 1)
+ * Other arguments, workspace and errors as ls_replay_attn_fwd; offsets that
+ * are not strictly increasing from 0 to R give LS_ERR_INVALID_ARG. */
+ls_status ls_replay_attn_fwd_members(const ls_attn_shape* shape, const ls_page_table* pt,
+                                     int32_t num_members, const int32_t* member_offsets,
+                                     const int32_t* member_offsets_dev, const void* q,
+                                     const void* k_pool, const void* v_pool,
+                                     const void* k_resp, const void* v_resp,
+                                     float* part_o, float* part_m, float* part_l,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* ls_lse_merge -- exact composition of partial attention (the pages' global
  * LSE/output merge of the CP8 shards; LongStraw review page, section 7 mind map).
  * For each row: M = max_c m_c, w_c = l_c * exp(m_c - M), L = sum_c w_c,

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     ls_replay_attn_bwd,
     ls_replay_attn_bwd_workspace,
     ls_replay_attn_fwd,
+    ls_replay_attn_fwd_members,
     ls_replay_attn_fwd_workspace,
     ls_status_string,
     ls_timing_enable,
@@ -38,4 +39,5 @@ from .replay import (  # noqa: F401
     replay_forward,
     replay_group,
     replay_member,
+    score_group,
 )

@@ -27,7 +27,7 @@ PAGE_SIZE = 256
 EXPORTS = (
     "ls_status_string", "ls_version", "ls_kv_page_table",
     "ls_replay_attn_fwd_workspace", "ls_replay_attn_bwd_workspace",
-    "ls_replay_attn_fwd", "ls_lse_merge", "ls_replay_attn_bwd",
+    "ls_replay_attn_fwd", "ls_replay_attn_fwd_members", "ls_lse_merge", "ls_replay_attn_bwd",
     "ls_timing_enable", "ls_timing_reset", "ls_timing_read",
 )
 
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
         "ls_replay_attn_fwd_workspace": (SZ, [P, P]),
         "ls_replay_attn_bwd_workspace": (SZ, [P, P]),
         "ls_replay_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "ls_replay_attn_fwd_members": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "ls_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P, P]),
         "ls_replay_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "ls_timing_enable": (I32, [I32]),
@@ -171,6 +172,24 @@ def ls_replay_attn_fwd(shape: AttnShape, pt: PageTable, q, k_pool, v_pool, k_res
         _ptr(part_o, f32, "part_o"), _ptr(part_m, f32, "part_m"), _ptr(part_l, f32, "part_l"),
         _ptr(workspace), ws_bytes, _stream(stream))
     _check("ls_replay_attn_fwd", st)
+
+
+def ls_replay_attn_fwd_members(shape: AttnShape, pt: PageTable, member_offsets, member_offsets_dev,
+                               q, k_pool, v_pool, k_resp, v_resp, part_o, part_m, part_l,
+                               workspace=None, stream=None) -> None:
+    """``member_offsets``: host int32 numpy array [G+1]; ``member_offsets_dev``: its device copy
+    (an int32 tensor), or None for one member."""
+    bf, f32 = torch.bfloat16, torch.float32
+    offs = np.ascontiguousarray(member_offsets, dtype=np.int32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev_ptr = 0 if member_offsets_dev is None else _ptr(member_offsets_dev, torch.int32, "member_offsets_dev")
+    st = lib().ls_replay_attn_fwd_members(
+        ctypes.byref(shape), ctypes.byref(pt), int(offs.size - 1), offs.ctypes.data, dev_ptr,
+        _ptr(q, bf, "q"), _ptr(k_pool, bf, "k_pool"), _ptr(v_pool, bf, "v_pool"),
+        _ptr(k_resp, bf, "k_resp"), _ptr(v_resp, bf, "v_resp"), _ptr(part_o, f32, "part_o"),
+        _ptr(part_m, f32, "part_m"), _ptr(part_l, f32, "part_l"), _ptr(workspace), ws_bytes,
+        _stream(stream))
+    _check("ls_replay_attn_fwd_members", st)
 
 
 def ls_lse_merge(num_parts: int, rows: int, head_dim: int, part_o, part_m, part_l, o_bf16, lse,

@@ -179,6 +179,79 @@ size_t bwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt) {
          kv_part_bytes(sh);
 }
 
+ls_status fwd_impl(const ls_attn_shape* sh, const ls_page_table* pt, int32_t nmem,
+                   const int32_t* moffs_dev, const void* q,
+                             const void* k_pool, const void* v_pool, const void* k_resp,
+                             const void* v_resp, float* part_o, float* part_m, float* part_l,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  ls_status st = check_shape(sh);
+  if (st != LS_OK) return st;
+  if ((st = check_table(sh, pt)) != LS_OK) return st;
+  if (!q || !k_resp || !v_resp || !part_o || !part_m || !part_l) return LS_ERR_INVALID_ARG;
+  if (pt->num_pages > 0 && (!k_pool || !v_pool)) return LS_ERR_INVALID_ARG;
+  for (const void* p : {q, k_pool, v_pool, k_resp, v_resp, (const void*)part_o,
+                        (const void*)part_m, (const void*)part_l, (const void*)ws})
+    if (p && !aligned16(p)) return LS_ERR_INVALID_ARG;
+  const size_t need = fwd_ws_bytes(*sh, *pt);
+  if (need > 0 && (!ws || ws_bytes < need)) return LS_ERR_WORKSPACE;
+  if (need == 0) ws = nullptr;
+
+  const Plan plan = plan_prompt(*sh, *pt, kFwdRows);
+  const size_t rows = (size_t)sh->num_q_heads * sh->resp_len;
+  const int d = sh->head_dim;
+  AttnArgs a = base_args(*sh, *pt, q, k_pool, v_pool);
+  a.chunks = plan.chunks;
+  a.chunk_pages = plan.chunk_pages;
+  a.mtiles = plan.mtiles;
+
+  char* w = static_cast<char*>(ws);
+  int32_t* phys = reinterpret_cast<int32_t*>(w);
+  w += phys_bytes(*pt);
+  a.phys = phys;
+  if (pt->num_pages > 0) {
+    st = run("resolve_pages", stream, [&] {
+      return launch_resolve_pages(pt->num_pages, pt->num_phys_pages, pt->order, pt->l2p, phys,
+                                  stream);
+    });
+    if (st != LS_OK) return st;
+  }
+  float *wo = part_o, *wm = part_m, *wl = part_l;
+  if (plan.chunks > 1) {
+    wo = reinterpret_cast<float*>(w);
+    w += round_up((size_t)plan.units * rows * d * 4, 256);
+    wm = reinterpret_cast<float*>(w);
+    w += round_up((size_t)plan.units * rows * 4, 256);
+    wl = reinterpret_cast<float*>(w);
+  }
+  // prompt splits (or their chunks)
+  a.o = wo;
+  a.m = wm;
+  a.l = wl;
+  a.slot_base = 0;
+  const int grid = plan.units * sh->num_kv_heads * plan.mtiles;
+  st = run("fwd_prompt", stream, [&] { return launch_fwd(a, d, false, grid, stream); });
+  if (st != LS_OK) return st;
+  if (plan.chunks > 1) {
+    st = run("fwd_combine", stream, [&] {
+      return launch_merge(pt->num_splits, plan.chunks, (int64_t)rows, d, wo, wm, wl, false,
+                          part_o, part_m, part_l, stream);
+    });
+    if (st != LS_OK) return st;
+  }
+  // causal response block -> part S
+  AttnArgs r = a;
+  r.k = static_cast<const uint16_t*>(k_resp);
+  r.v = static_cast<const uint16_t*>(v_resp);
+  r.o = part_o;
+  r.m = part_m;
+  r.l = part_l;
+  r.slot_base = pt->num_splits;
+  r.moffs = nmem > 1 ? moffs_dev : nullptr;
+  r.nmembers = nmem;
+  const int rgrid = sh->num_kv_heads * plan.mtiles;
+  return run("fwd_resp", stream, [&] { return launch_fwd(r, d, true, rgrid, stream); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -260,70 +333,25 @@ ls_status ls_replay_attn_fwd(const ls_attn_shape* sh, const ls_page_table* pt, c
                              const void* k_pool, const void* v_pool, const void* k_resp,
                              const void* v_resp, float* part_o, float* part_m, float* part_l,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
-  ls_status st = check_shape(sh);
-  if (st != LS_OK) return st;
-  if ((st = check_table(sh, pt)) != LS_OK) return st;
-  if (!q || !k_resp || !v_resp || !part_o || !part_m || !part_l) return LS_ERR_INVALID_ARG;
-  if (pt->num_pages > 0 && (!k_pool || !v_pool)) return LS_ERR_INVALID_ARG;
-  for (const void* p : {q, k_pool, v_pool, k_resp, v_resp, (const void*)part_o,
-                        (const void*)part_m, (const void*)part_l, (const void*)ws})
-    if (p && !aligned16(p)) return LS_ERR_INVALID_ARG;
-  const size_t need = fwd_ws_bytes(*sh, *pt);
-  if (need > 0 && (!ws || ws_bytes < need)) return LS_ERR_WORKSPACE;
-  if (need == 0) ws = nullptr;
+  return fwd_impl(sh, pt, 1, nullptr, q, k_pool, v_pool, k_resp, v_resp, part_o, part_m, part_l,
+                  ws, ws_bytes, stream);
+}
 
-  const Plan plan = plan_prompt(*sh, *pt, kFwdRows);
-  const size_t rows = (size_t)sh->num_q_heads * sh->resp_len;
-  const int d = sh->head_dim;
-  AttnArgs a = base_args(*sh, *pt, q, k_pool, v_pool);
-  a.chunks = plan.chunks;
-  a.chunk_pages = plan.chunk_pages;
-  a.mtiles = plan.mtiles;
-
-  char* w = static_cast<char*>(ws);
-  int32_t* phys = reinterpret_cast<int32_t*>(w);
-  w += phys_bytes(*pt);
-  a.phys = phys;
-  if (pt->num_pages > 0) {
-    st = run("resolve_pages", stream, [&] {
-      return launch_resolve_pages(pt->num_pages, pt->num_phys_pages, pt->order, pt->l2p, phys,
-                                  stream);
-    });
-    if (st != LS_OK) return st;
-  }
-  float *wo = part_o, *wm = part_m, *wl = part_l;
-  if (plan.chunks > 1) {
-    wo = reinterpret_cast<float*>(w);
-    w += round_up((size_t)plan.units * rows * d * 4, 256);
-    wm = reinterpret_cast<float*>(w);
-    w += round_up((size_t)plan.units * rows * 4, 256);
-    wl = reinterpret_cast<float*>(w);
-  }
-  // prompt splits (or their chunks)
-  a.o = wo;
-  a.m = wm;
-  a.l = wl;
-  a.slot_base = 0;
-  const int grid = plan.units * sh->num_kv_heads * plan.mtiles;
-  st = run("fwd_prompt", stream, [&] { return launch_fwd(a, d, false, grid, stream); });
-  if (st != LS_OK) return st;
-  if (plan.chunks > 1) {
-    st = run("fwd_combine", stream, [&] {
-      return launch_merge(pt->num_splits, plan.chunks, (int64_t)rows, d, wo, wm, wl, false,
-                          part_o, part_m, part_l, stream);
-    });
-    if (st != LS_OK) return st;
-  }
-  // causal response block -> part S
-  AttnArgs r = a;
-  r.k = static_cast<const uint16_t*>(k_resp);
-  r.v = static_cast<const uint16_t*>(v_resp);
-  r.o = part_o;
-  r.m = part_m;
-  r.l = part_l;
-  r.slot_base = pt->num_splits;
-  const int rgrid = sh->num_kv_heads * plan.mtiles;
-  return run("fwd_resp", stream, [&] { return launch_fwd(r, d, true, rgrid, stream); });
+ls_status ls_replay_attn_fwd_members(const ls_attn_shape* sh, const ls_page_table* pt,
+                                     int32_t num_members, const int32_t* member_offsets,
+                                     const int32_t* member_offsets_dev, const void* q,
+                                     const void* k_pool, const void* v_pool, const void* k_resp,
+                                     const void* v_resp, float* part_o, float* part_m,
+                                     float* part_l, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (!sh || num_members < 1 || !member_offsets) return LS_ERR_INVALID_ARG;
+  if (num_members > 1 && !member_offsets_dev) return LS_ERR_INVALID_ARG;
+  if (member_offsets[0] != 0 || member_offsets[num_members] != sh->resp_len)
+    return LS_ERR_INVALID_ARG;
+  for (int32_t k = 0; k < num_members; ++k)
+    if (member_offsets[k + 1] <= member_offsets[k]) return LS_ERR_INVALID_ARG;
+  return fwd_impl(sh, pt, num_members, member_offsets_dev, q, k_pool, v_pool, k_resp, v_resp,
+                  part_o, part_m, part_l, ws, ws_bytes, stream);
 }
 
 ls_status ls_lse_merge(int32_t num_parts, int64_t rows, int32_t head_dim, const float* part_o,

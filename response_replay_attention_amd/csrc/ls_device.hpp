@@ -313,18 +313,34 @@ __device__ __forceinline__ int ld_table(const int32_t* t, int i) {
 // do.  A page id out of range reads block 0 of the pool in the unmasked loop
 // and is skipped in the masked one, so a corrupted device page table gives
 // wrong numbers but never an out-of-bounds access.
+// First response row of the member that holds response row i (members are
+// consecutive row ranges; one member when there is no offset table).
+__device__ __forceinline__ int member_start(const AttnArgs& a, int i) {
+  int s = 0;
+  if (a.moffs)
+    for (int k = 1; k < a.nmembers; ++k) {
+      const int o = ld_table(a.moffs, k);
+      s = (i >= o) ? o : s;
+    }
+  return s;
+}
+
 template <int D, bool RESP>
 struct KeyWalk {
   const AttnArgs& a;
-  int kv, p0, nblocks, nfull;
+  int kv, p0, nblocks, nfull, jfirst;
   // unit = split*chunks + chunk (paged); rows [m0, m0 + rows) of the group
   __device__ __forceinline__ KeyWalk(const AttnArgs& args, int kv_, int unit, int m0, int rows)
-      : a(args), kv(kv_), p0(0), nblocks(0), nfull(0) {
+      : a(args), kv(kv_), p0(0), nblocks(0), nfull(0), jfirst(0) {
     const int GR = (a.hq / a.hkv) * a.R;
     if (RESP) {
+      // keys [first key of the first row's member, last row] cover every row
+      // of the tile when it stays inside one query head; else all keys
       const int mlast = min(m0 + rows, GR) - 1;
-      const int imax = (m0 / a.R != mlast / a.R) ? a.R - 1 : mlast % a.R;
+      const bool one_head = m0 / a.R == mlast / a.R;
+      const int imax = one_head ? mlast % a.R : a.R - 1;
       nblocks = (imax + kBN) / kBN;
+      jfirst = one_head ? member_start(a, m0 % a.R) / kBN : 0;
       nfull = 0;
     } else {
       const int c = unit / a.chunks, k = unit - c * a.chunks;

@@ -93,8 +93,9 @@ __device__ __forceinline__ void block_pv(f32x16 (&acc)[D / 32], const LanesX<D>&
 // block's max when `first`), so the softmax needs no per-block maximum: the
 // lane's running maximum of raw scores (mlane) is checked against the shift
 // once the range is done.
-// MASK: keys at index >= nvalid, and (response block) keys after the query's
-// own position qi, are masked; COPY: issue the block copies.
+// MASK: keys at index >= nvalid, and (response block) keys before kmin or
+// after kmax (block-relative: the row's member start and its own position)
+// are masked; COPY: issue the block copies.
 template <int D, bool MASK, bool COPY>
 __device__ __forceinline__ void fwd_step(const LanesX<D>& tl, const BlockLoader<D, kFwdWaves>& ldr,
                                          const uint16_t* kt, const uint16_t* vt,
@@ -102,7 +103,7 @@ __device__ __forceinline__ void fwd_step(const LanesX<D>& tl, const BlockLoader<
                                          float s2, bool first, float& mu, float& mlane,
                                          float& lsum, uint32_t kdst, i32x4 kdesc, uint32_t vdst,
                                          i32x4 vdesc, int nvalid = kBN, int kmax = 0x7fffffff,
-                                         int hf = 0) {
+                                         int hf = 0, int kmin = -0x7fffffff) {
   constexpr int NS = D / 16;   // score MFMAs per step = PV MFMAs per step
   constexpr int NMT = D / 32;  // 32-wide d tiles of O^T
   constexpr int PF = 1;        // LDS prefetch distance, in MFMAs
@@ -128,12 +129,16 @@ __device__ __forceinline__ void fwd_step(const LanesX<D>& tl, const BlockLoader<
     __builtin_amdgcn_sched_barrier(0);
   }
   if (MASK) {
-    // key crow(r, hf) = 4*hf + 8*(r/4) + r%4 of the block is visible iff it is
-    // < nvalid and <= kmax; compared as compile-time row offsets against two
-    // per-lane thresholds, so no key index is kept in a register
-    const int lim = min(nvalid - 1, kmax) - 4 * hf;
+    // key crow(r, hf) = 4*hf + 8*(r/4) + r%4 of the block is visible iff
+    // kmin <= key <= min(nvalid - 1, kmax); compared as compile-time row
+    // offsets against per-lane thresholds, so no key index is kept in a register
+    const int hi = min(nvalid - 1, kmax) - 4 * hf;
+    const int lo = max(kmin, -0x7fff) - 4 * hf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) <= lim) ? s[r] : -kInf;
+    for (int r = 0; r < 16; ++r) {
+      const int c = 8 * (r >> 2) + (r & 3);
+      s[r] = (c <= hi && c >= lo) ? s[r] : -kInf;
+    }
   }
   if (first) {
     float mx = s[0];
@@ -206,6 +211,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   // group are computed on a copy of its last row and never stored.
   bf16x8 qr[D / 16];
   const int qi = m % a.R;
+  const int qlo = RESP ? member_start(a, qi) : 0;  // first visible response key
   {
     const uint16_t* qp = a.q + (row0 + min(m, GR - 1)) * D + 8 * hf;
 #pragma unroll
@@ -297,7 +303,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
     // ---- masked blocks (partial last prompt page; the causal response block)
     {
       float mlane = -kInf;
-      for (int j = nfull; j < nblocks; ++j) {
+      for (int j = max(nfull, walk.jfirst); j < nblocks; ++j) {
         int nv, key0;
         const size_t off = walk.block(j, nv, key0);
         if (nv > 0) {
@@ -311,7 +317,8 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
           const i32x4 none = {0, 0, 0, 0};
           fwd_step<D, true, false>(tl, ldr, k0, v0, qr, acc, a.s2, pass0 && mref == -kInf, mref,
                                    mlane, lsum, 0, none, 0, none, nv,
-                                   RESP ? qi - key0 : 0x7fffffff, hf);
+                                   RESP ? qi - key0 : 0x7fffffff, hf,
+                                   RESP ? qlo - key0 : -0x7fffffff);
         }
         __syncthreads();  // tiles are rewritten by the next block
       }

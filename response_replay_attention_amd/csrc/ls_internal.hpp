@@ -28,6 +28,8 @@ struct AttnArgs {
   const int32_t* order;   // device split-major page list (paged only)
   const int32_t* offs;    // device split offsets (paged only)
   const int32_t* phys;    // device physical slot of each page of `order` (-1: bad id)
+  const int32_t* moffs;   // device member row offsets [nmembers + 1] (response block;
+  int32_t nmembers;       //   null: one member): keys are visible only inside a member
   int64_t prompt_len;
   int32_t num_pages, num_phys, chunks, chunk_pages;
   int32_t hq, hkv, R, mtiles;

@@ -93,6 +93,39 @@ def replay_forward(cache: PromptCache, q, k_resp, v_resp, scale=None, stream=Non
     return ForwardResult(o, lse, part_o, part_m, part_l)
 
 
+def score_group(cache: PromptCache, members: Iterable["Member"], scale=None, stream=None) -> List:
+    """Forward-only scoring of a whole group in one pass over the prompt: the
+    members' queries and response K/V are stacked along the response axis, the
+    prompt splits are computed once for all of them (every K/V block serves
+    every member's rows), the response block keeps each member to its own
+    keys, and the merge yields every member's O and LSE.  Returns one
+    ``(o, lse)`` pair per member (views into the stacked outputs)."""
+    members = list(members)
+    lens = [int(m.q.shape[1]) for m in members]
+    offs = np.zeros(len(members) + 1, dtype=np.int32)
+    offs[1:] = np.cumsum(lens)
+    q = torch.cat([m.q for m in members], dim=1).contiguous()
+    k_resp = torch.cat([m.k_resp for m in members], dim=1).contiguous()
+    v_resp = torch.cat([m.v_resp for m in members], dim=1).contiguous()
+    sh = cache.shape(q, scale)
+    hq, r, d = q.shape
+    dev = q.device
+    nparts = cache.num_splits + 1
+    part_o = torch.empty(nparts, hq, r, d, dtype=torch.float32, device=dev)
+    part_m = torch.empty(nparts, hq, r, dtype=torch.float32, device=dev)
+    part_l = torch.empty(nparts, hq, r, dtype=torch.float32, device=dev)
+    wsb = B.ls_replay_attn_fwd_workspace(sh, cache.pt)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+    offs_dev = torch.from_numpy(offs).to(dev) if len(members) > 1 else None
+    B.ls_replay_attn_fwd_members(sh, cache.pt, offs, offs_dev, q, cache.k_pool, cache.v_pool,
+                                 k_resp, v_resp, part_o, part_m, part_l, ws, stream)
+    o = torch.empty(hq, r, d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(hq, r, dtype=torch.float32, device=dev)
+    B.ls_lse_merge(nparts, hq * r, d, part_o, part_m, part_l, o, lse, stream)
+    del ws, part_o, part_m, part_l
+    return [(o[:, offs[k]:offs[k + 1]], lse[:, offs[k]:offs[k + 1]]) for k in range(len(members))]
+
+
 def replay_backward(cache: PromptCache, q, k_resp, v_resp, o, lse, d_o, scale=None, stream=None):
     """Response-only backward: returns ``(dq, dk_resp, dv_resp)`` in fp32.
     The prompt pools get no gradient."""

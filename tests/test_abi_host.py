@@ -242,3 +242,37 @@ def test_merge_rejects(kw, status):
 def test_timing_read_unknown_kernel_is_empty():
     rra.ls_timing_reset()
     assert rra.ls_timing_read("no_such_kernel") == (0, 0.0)
+
+
+def _fwd_members(sh, pt, offs, dev=FAKE, num_members=None, **ptrs):
+    p = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, k_resp=FAKE, v_resp=FAKE, part_o=FAKE,
+             part_m=FAKE, part_l=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    p.update(ptrs)
+    o = np.ascontiguousarray(offs, dtype=np.int32)
+    g = o.size - 1 if num_members is None else num_members
+    return rra.lib().ls_replay_attn_fwd_members(
+        ctypes.byref(sh), ctypes.byref(pt), g, o.ctypes.data if o.size else None, dev, p["q"],
+        p["k_pool"], p["v_pool"], p["k_resp"], p["v_resp"], p["part_o"], p["part_m"],
+        p["part_l"], p["ws"], p["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("offs", [
+    [0, 64, 64],          # an empty member
+    [1, 32, 64],          # does not start at row 0
+    [0, 32, 63],          # does not end at resp_len
+    [0, 40, 32, 64],      # decreasing
+    [0, 65],              # past resp_len
+])
+def test_members_reject_bad_offsets(offs):
+    assert _fwd_members(_shape(), _table(), offs) == INVALID
+
+
+def test_members_reject_bad_counts_and_pointers():
+    sh, pt = _shape(), _table()
+    assert _fwd_members(sh, pt, [0, 64], num_members=0) == INVALID
+    assert _fwd_members(sh, pt, [0, 32, 64], dev=0) == INVALID     # no device copy for G > 1
+    assert _fwd_members(sh, pt, []) == INVALID                      # no host offsets
+    # the shared checks of ls_replay_attn_fwd still apply
+    assert _fwd_members(_shape(head_dim=64), pt, [0, 32, 64]) == UNSUPPORTED
+    assert _fwd_members(sh, pt, [0, 32, 64], q=FAKE + 2) == INVALID
+    assert _fwd_members(sh, pt, [0, 32, 64], ws_bytes=0) == WORKSPACE
