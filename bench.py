@@ -14,6 +14,9 @@ eight members (R = 512 ... 4096) over the shared prompt, `prompt_keys_per_s` cou
 times members, and the line also carries each member's time from one extra, untimed pass.
 ``--score`` times forward-only scoring instead: all members in one pass over the prompt
 (``ls_replay_attn_fwd_members``) and the merge, counting forward flops only.
+A name in ``replay_inputs.CAPTURE_WORKLOADS`` times the chunked capture of one full-attention
+layer instead: a step prefills the whole prompt chunk by chunk (each chunk's forward over the
+pages before it and itself, the merge, and the append of its pages); flops are the forward's.
 
 Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step
 (only unmasked scores counted: 4d flops per (head,row,key) forward; 6d per
@@ -38,7 +41,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
 DOMINANT = "bwd_prompt_dq"  # 60% of the algorithmic flops
 KERNELS = ("fwd_prompt", "fwd_combine", "fwd_resp", "lse_merge", "bwd_dot", "bwd_prompt_dq",
-           "bwd_resp_dq", "bwd_resp_dkdv", "kv_reduce", "dq_reduce")
+           "bwd_resp_dq", "bwd_resp_dkdv", "kv_reduce", "dq_reduce", "page_append")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_prompt_dq_traffic_prefix2M.md")
 
 
@@ -128,6 +131,148 @@ def cpu_baseline(shape, inp, seconds_hint: float = 20.0):
     }
 
 
+def capture_flops(shape) -> dict:
+    """Forward flops of the chunked capture: chunk [s, e) scores every earlier
+    position and, causally, itself."""
+    d, hq = shape.head_dim, shape.hq
+    out = {"fwd_prompt": 0, "fwd_resp": 0}
+    for s, e in shape.spans():
+        tc = e - s
+        out["fwd_prompt"] += 4 * d * hq * tc * s
+        out["fwd_resp"] += 4 * d * hq * tc * (tc + 1) // 2
+    return out
+
+
+def cpu_baseline_capture(shape, inp):
+    """The float64 oracle on the host: causal attention of the last rows of the
+    prompt (query heads of KV head 0) over every position before them."""
+    import numpy as np
+
+    import oracle
+    from replay_inputs import whole_prompt
+
+    g = shape.hq // shape.hkv
+    T = shape.total_len
+    # about 10 s of host work: ~6e7 (row x key) pairs per second measured
+    rows = max(1, min(512, (96 << 20) // T))
+    t0 = time.perf_counter()
+    q = whole_prompt([(c[0][:g], c[1][:1], c[2][:1]) for c in inp["chunks"]], 0)[:, T - rows:].cpu()
+    k = whole_prompt([(None, c[1][:1], None) for c in inp["chunks"]], 1).cpu()
+    v = whole_prompt([(None, None, c[2][:1]) for c in inp["chunks"]], 2).cpu()
+    # the sampled rows are the last ones: give the oracle the sequence's keys
+    # as the prompt and the sampled rows' own keys as the causal block
+    kp, vp = k[:, : T - rows], v[:, : T - rows]
+    kr, vr = k[:, T - rows:], v[:, T - rows:]
+    sel = np.tile(np.arange(rows), (g, 1))
+    t1 = time.perf_counter()
+    oracle.replay_forward(q, kp, vp, kr, vr, shape.scale, rows=sel)
+    t2 = time.perf_counter()
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    n = g * rows
+    keys = sum(T - rows + i + 1 for i in range(rows)) * g
+    secs = t2 - t1
+    return {
+        "value": 4 * shape.head_dim * keys / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 oracle forward of {n} rows (KV head 0: {g} query heads x the last {rows} "
+                   f"positions) over every earlier position of the {T}-position prompt; "
+                   f"{secs:.1f} s compute (+{t1 - t0:.1f} s to gather inputs)"),
+    }
+
+
+def bench_capture(args, shape) -> int:
+    import torch
+
+    from replay_inputs import make_capture_inputs
+    from response_replay_attention_amd import (capture_prefill, ls_timing_enable, ls_timing_read,
+                                               ls_timing_reset)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_capture_inputs(shape, args.seed, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        capture_prefill(inp["chunks"], inp["k_pool"], inp["v_pool"], inp["slots"],
+                        shape.num_splits, shape.policy, shape.block_pages, shape.scale,
+                        consume=lambda i, o, lse: None)
+
+    for _ in range(args.warmup):
+        step()
+    ls_timing_reset()
+    ls_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ls_timing_enable(False)
+    kern = {}
+    for k in KERNELS:
+        n, ms = ls_timing_read(k)
+        if n:
+            kern[k] = {"launches": n, "avg_ms": ms / n, "total_ms": ms}
+    fl = capture_flops(shape)
+    step_flops = sum(fl.values())
+    tflops = step_flops * args.steps / elapsed / 1e12
+    # launches of the dominant kernel differ in size (the prompt grows chunk by
+    # chunk): its achieved rate is all its flops over all its time
+    dom = kern.get("fwd_prompt", {"total_ms": float("nan"), "launches": 0})
+    achieved = fl["fwd_prompt"] * args.steps / (dom["total_ms"] * 1e-3) / 1e12
+    app = kern.get("page_append", {"avg_ms": float("nan")})
+    chunk_bytes = 2 * shape.hkv * shape.chunk * shape.head_dim * 2  # K and V, bf16
+    out = {
+        "metric": "chunked capture (forward) TFLOP/s & positions/s; % bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": shape.name,
+            "q_heads": shape.hq, "kv_heads": shape.hkv, "head_dim": shape.head_dim,
+            "prompt_len": shape.total_len, "chunk": shape.chunk, "splits": shape.num_splits,
+            "page_size": 256, "parallelism": "1 GPU; CP ranks emulated as page splits",
+        },
+        "positions_per_s": round(shape.total_len * args.steps / elapsed, 1),
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "kernel": "fwd_prompt",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "source_digest": source_digest(),
+        },
+        # the page writer is HBM-bound: K and V of a whole chunk read once and written once
+        "page_append": {
+            "avg_ms": round(app["avg_ms"], 4),
+            "achieved_GBps": round(2 * chunk_bytes / (app["avg_ms"] * 1e-3) / 1e9, 1),
+            "peak_GBps": PEAK_HBM_GBPS,
+        },
+        "kernels_avg_ms": {k: round(v["avg_ms"], 4) for k, v in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_capture(shape, inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,7 +296,10 @@ def main() -> int:
 
     import torch
 
-    from replay_inputs import GROUP_2M, GROUP_2M_RESP_LENS, WORKLOADS, make_inputs, make_response
+    from replay_inputs import (CAPTURE_WORKLOADS, GROUP_2M, GROUP_2M_RESP_LENS, WORKLOADS,
+                               make_inputs, make_response)
+    if args.workload in CAPTURE_WORKLOADS:
+        return bench_capture(args, CAPTURE_WORKLOADS[args.workload])
     from response_replay_attention_amd import (Member, PromptCache, ls_timing_enable,
                                                ls_timing_read, ls_timing_reset, replay_backward,
                                                replay_forward, replay_group, score_group)

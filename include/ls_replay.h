@@ -192,6 +192,34 @@ ls_status ls_replay_attn_fwd_members(const ls_attn_shape* shape, const ls_page_t
                                      void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* ls_kv_page_append -- the capture-side page writer: stores the K and V of
+ * T freshly prefilled prompt tokens as compact pages of the pool (the shared
+ * prompt is prefilled once without a graph and only the per-token K/V of the
+ * full-attention layers is kept, in pages; DeepRead summary page, "Method";
+ * LongStraw review page, section 2, items 1 and 2; the prefill runs in
+ * 4096-token chunks, LongStraw review page, section 3).  The chunk's first
+ * token is the first row of a page, so token t of the chunk lands in pool
+ * slot slots[t / 256], row t % 256, for every KV head:
+ *   k_pool[slots[t/256], h, t%256, :] = k_chunk[h, t, :]   (same for v).
+ * Rows of the chunk's last page past T are left untouched (the page table's
+ * prompt_len masks them).
+ *   num_kv_heads    Hkv >= 1;  head_dim d in {128, 256};  tokens T >= 1
+ *   k_chunk, v_chunk   device bf16 [Hkv, T, d], 16-byte aligned
+ *   slots_host      host int32 [ceil(T/256)]: pool slot of each new page
+ *   slots_dev       device copy of slots_host (read by the kernel)
+ *   k_pool, v_pool  device bf16 [num_phys_pages, Hkv, 256, d], 16-byte aligned
+ *   num_phys_pages  pool slots; every slot must lie in [0, num_phys_pages)
+ *                   and appear once (a compact page is its own allocation).
+ * Nothing is allocated; the copy is enqueued on stream.  The caller records
+ * the new pages in the logical->physical map it passes to ls_kv_page_table.
+ * Errors: LS_ERR_INVALID_ARG (counts, NULL or misaligned pointers),
+ * LS_ERR_UNSUPPORTED (d, or Hkv*T*d >= 2^31), LS_ERR_PAGE_RANGE (slot out of
+ * range or repeated), LS_ERR_HIP. */
+ls_status ls_kv_page_append(int32_t num_kv_heads, int32_t head_dim, int32_t tokens,
+                            const void* k_chunk, const void* v_chunk, const int32_t* slots_host,
+                            const int32_t* slots_dev, void* k_pool, void* v_pool,
+                            int32_t num_phys_pages, hipStream_t stream);
+
 /* ls_lse_merge -- exact composition of partial attention (the pages' global
  * LSE/output merge of the CP8 shards; LongStraw review page, section 7 mind map).
  * For each row: M = max_c m_c, w_c = l_c * exp(m_c - M), L = sum_c w_c,

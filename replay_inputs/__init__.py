@@ -91,6 +91,75 @@ STRESS_4M = ReplayShape("stress_24x4_d256_p4456448_r2048_s16", 24, 4, 256, 4_456
 WORKLOADS = {s.name: s for s in (TINY, SHARD_256K, FULL_2M, GROUP_2M, STRESS_4M)}
 
 
+@dataclasses.dataclass(frozen=True)
+class CaptureShape:
+    """Chunked capture of one full-attention layer: ``total_len`` prompt
+    positions prefilled ``chunk`` at a time (the pages' chunks are 4096
+    tokens), each chunk attending to the pages before it, dealt to
+    ``num_splits`` splits, and causally to itself."""
+
+    name: str
+    hq: int
+    hkv: int
+    head_dim: int
+    total_len: int
+    chunk: int
+    num_splits: int
+    policy: int = SPLIT_CONTIGUOUS
+    block_pages: int = 1
+    extra_phys_pages: int = 3
+
+    @property
+    def num_pages(self) -> int:
+        return (self.total_len + PAGE_SIZE - 1) // PAGE_SIZE
+
+    @property
+    def num_phys_pages(self) -> int:
+        return self.num_pages + self.extra_phys_pages
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def spans(self) -> List[tuple]:
+        return [(s, min(self.total_len, s + self.chunk)) for s in range(0, self.total_len, self.chunk)]
+
+
+CAPTURE_256K = CaptureShape("capture_24x4_d256_p262144_c4096_s8", 24, 4, 256, 262_144, 4096, 8,
+                            SPLIT_BLOCK_CYCLIC, 1)
+CAPTURE_WORKLOADS = {CAPTURE_256K.name: CAPTURE_256K}
+
+
+def make_capture_inputs(shape: CaptureShape, seed: int, device="cpu") -> Dict[str, object]:
+    """Draw one capture problem: the whole prompt's projections ``q [Hq,T,d]``,
+    ``k/v [Hkv,T,d]`` (bf16) cut into contiguous per-chunk tensors
+    (``chunks``: list of ``(q, k, v)``), junk-filled pools
+    ``[num_phys, Hkv, 256, d]`` and ``slots`` (int32 CPU, a seeded injection of
+    the prompt's logical pages into the pool slots)."""
+    H, Hk, d, T = shape.hq, shape.hkv, shape.head_dim, shape.total_len
+    dev = torch.device(device)
+    full = {"q": _randn_bf16((H, T, d), _gen(seed, _T_Q, dev), dev),
+            "k": _randn_bf16((Hk, T, d), _gen(seed, _T_KR, dev), dev),
+            "v": _randn_bf16((Hk, T, d), _gen(seed, _T_VR, dev), dev)}
+    chunks = []
+    for s, e in shape.spans():
+        chunks.append(tuple(full[n][:, s:e].contiguous() for n in ("q", "k", "v")))
+    del full
+    pool_shape = (shape.num_phys_pages, Hk, PAGE_SIZE, d)
+    g = _gen(seed, _T_PERM, "cpu")
+    slots = torch.randperm(shape.num_phys_pages, generator=g)[: shape.num_pages].to(torch.int32)
+    return {"chunks": chunks,
+            "k_pool": _randn_bf16(pool_shape, _gen(seed, _T_KP, dev), dev),
+            "v_pool": _randn_bf16(pool_shape, _gen(seed, _T_VP, dev), dev),
+            "slots": slots.contiguous()}
+
+
+def whole_prompt(chunks, index: int) -> torch.Tensor:
+    """Concatenate one projection (0 = q, 1 = k, 2 = v) of every chunk back into
+    ``[H, T, d]`` along the token axis.  Pure indexing."""
+    return torch.cat([c[index] for c in chunks], dim=1)
+
+
 def _gen(seed: int, tid: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed) * 16 + tid)

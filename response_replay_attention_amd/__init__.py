@@ -5,7 +5,8 @@ paged prompt K/V cache, split over prompt pages and merged through
 log-sum-exp statistics, with a response-only backward (no prompt K/V
 gradient).  The arithmetic lives in ``libls_replay.so`` (hand-written HIP
 kernels behind the C ABI of ``include/ls_replay.h``); this package is its
-binding and a small replay driver.
+binding, a small replay driver and the chunked capture that writes the
+prompt's pages.
 """
 from .binding import (  # noqa: F401
     EXPORTS,
@@ -17,6 +18,7 @@ from .binding import (  # noqa: F401
     LsError,
     PageTable,
     lib,
+    ls_kv_page_append,
     ls_kv_page_table,
     ls_lse_merge,
     ls_replay_attn_bwd,
@@ -32,9 +34,11 @@ from .binding import (  # noqa: F401
     make_shape,
 )
 from .replay import (  # noqa: F401
+    CaptureResult,
     ForwardResult,
     Member,
     PromptCache,
+    capture_prefill,
     replay_backward,
     replay_forward,
     replay_group,

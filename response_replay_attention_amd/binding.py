@@ -27,7 +27,8 @@ PAGE_SIZE = 256
 EXPORTS = (
     "ls_status_string", "ls_version", "ls_kv_page_table",
     "ls_replay_attn_fwd_workspace", "ls_replay_attn_bwd_workspace",
-    "ls_replay_attn_fwd", "ls_replay_attn_fwd_members", "ls_lse_merge", "ls_replay_attn_bwd",
+    "ls_replay_attn_fwd", "ls_replay_attn_fwd_members", "ls_kv_page_append", "ls_lse_merge",
+    "ls_replay_attn_bwd",
     "ls_timing_enable", "ls_timing_reset", "ls_timing_read",
 )
 
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "ls_replay_attn_bwd_workspace": (SZ, [P, P]),
         "ls_replay_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "ls_replay_attn_fwd_members": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "ls_kv_page_append": (I32, [I32, I32, I32, P, P, P, P, P, P, I32, P]),
         "ls_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P, P]),
         "ls_replay_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "ls_timing_enable": (I32, [I32]),
@@ -190,6 +192,21 @@ def ls_replay_attn_fwd_members(shape: AttnShape, pt: PageTable, member_offsets, 
         _ptr(part_m, f32, "part_m"), _ptr(part_l, f32, "part_l"), _ptr(workspace), ws_bytes,
         _stream(stream))
     _check("ls_replay_attn_fwd_members", st)
+
+
+def ls_kv_page_append(k_chunk, v_chunk, slots, slots_dev, k_pool, v_pool, stream=None) -> None:
+    """``k_chunk``/``v_chunk``: bf16 [Hkv, T, d]; ``slots``: host int32 [ceil(T/256)];
+    ``slots_dev``: its device copy (int32 tensor); pools bf16 [num_phys, Hkv, 256, d]."""
+    bf = torch.bfloat16
+    hkv, tokens, d = (int(x) for x in k_chunk.shape)
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    if sl.size != (tokens + PAGE_SIZE - 1) // PAGE_SIZE:
+        raise ValueError(f"slots: expected {(tokens + PAGE_SIZE - 1) // PAGE_SIZE} entries, got {sl.size}")
+    st = lib().ls_kv_page_append(
+        hkv, d, tokens, _ptr(k_chunk, bf, "k_chunk"), _ptr(v_chunk, bf, "v_chunk"),
+        sl.ctypes.data, _ptr(slots_dev, torch.int32, "slots_dev"), _ptr(k_pool, bf, "k_pool"),
+        _ptr(v_pool, bf, "v_pool"), int(k_pool.shape[0]), _stream(stream))
+    _check("ls_kv_page_append", st)
 
 
 def ls_lse_merge(num_parts: int, rows: int, head_dim: int, part_o, part_m, part_l, o_bf16, lse,

@@ -354,6 +354,30 @@ ls_status ls_replay_attn_fwd_members(const ls_attn_shape* sh, const ls_page_tabl
                   part_o, part_m, part_l, ws, ws_bytes, stream);
 }
 
+ls_status ls_kv_page_append(int32_t num_kv_heads, int32_t head_dim, int32_t tokens,
+                            const void* k_chunk, const void* v_chunk, const int32_t* slots_host,
+                            const int32_t* slots_dev, void* k_pool, void* v_pool,
+                            int32_t num_phys_pages, hipStream_t stream) {
+  if (num_kv_heads < 1 || tokens < 1 || num_phys_pages < 1) return LS_ERR_INVALID_ARG;
+  if (head_dim != 128 && head_dim != 256) return LS_ERR_UNSUPPORTED;
+  if (!slots_host || !slots_dev) return LS_ERR_INVALID_ARG;
+  for (const void* p : {k_chunk, v_chunk, static_cast<const void*>(k_pool),
+                        static_cast<const void*>(v_pool)})
+    if (!p || !aligned16(p)) return LS_ERR_INVALID_ARG;
+  if ((int64_t)num_kv_heads * tokens * head_dim >= (int64_t(1) << 31)) return LS_ERR_UNSUPPORTED;
+  const int32_t npages = (tokens + kPage - 1) / kPage;
+  std::vector<char> seen(num_phys_pages, 0);
+  for (int32_t p = 0; p < npages; ++p) {
+    const int32_t sl = slots_host[p];
+    if (sl < 0 || sl >= num_phys_pages || seen[sl]) return LS_ERR_PAGE_RANGE;
+    seen[sl] = 1;
+  }
+  return run("page_append", stream, [&] {
+    return launch_page_append(num_kv_heads, head_dim, tokens, num_phys_pages, k_chunk, v_chunk,
+                              slots_dev, k_pool, v_pool, stream);
+  });
+}
+
 ls_status ls_lse_merge(int32_t num_parts, int64_t rows, int32_t head_dim, const float* part_o,
                        const float* part_m, const float* part_l, void* o_bf16, float* lse,
                        hipStream_t stream) {

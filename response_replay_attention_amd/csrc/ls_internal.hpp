@@ -68,6 +68,9 @@ hipError_t launch_bwd_dot(int64_t rows, int head_dim, const uint16_t* d_o, const
 // phys[i] = l2p[order[i]] for i < num_pages, -1 where either id is out of range.
 hipError_t launch_resolve_pages(int32_t num_pages, int32_t num_phys, const int32_t* order,
                                 const int32_t* l2p, int32_t* phys, hipStream_t s);
+hipError_t launch_page_append(int hkv, int head_dim, int tokens, int num_phys,
+                              const void* k_chunk, const void* v_chunk, const int32_t* slots,
+                              void* k_pool, void* v_pool, hipStream_t s);
 hipError_t launch_dq_reduce(int nslots, int64_t elems, const float* slots, float* dq,
                             hipStream_t s);
 

@@ -166,6 +166,45 @@ hipError_t launch_kv_reduce(int g, int64_t elems, const float* part, float* dv, 
   return hipGetLastError();
 }
 
+// Page writer: K and V of one chunk of T captured tokens ([Hkv, T, d], row
+// stride d) into pool slots ([phys, Hkv, 256, d]); token t of the chunk goes to
+// slot slots[t / 256], row t % 256.  16-byte units, grid-stride; positions
+// past T in the chunk's last page are not written, nor is a page whose slot
+// lies outside the pool.
+__global__ void __launch_bounds__(256) k_page_append(int hkv, int d8, int tokens, int64_t n16,
+                                                     int num_phys,
+                                                     const uint4* __restrict__ kc,
+                                                     const uint4* __restrict__ vc,
+                                                     const int32_t* __restrict__ slots,
+                                                     uint4* __restrict__ kp, uint4* __restrict__ vp) {
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n16;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(u % d8);
+    const int64_t r = u / d8;             // source row kv * T + t
+    const int t = (int)(r % tokens);
+    const int kv = (int)(r / tokens);
+    const int slot = slots[t >> 8];
+    if (slot < 0 || slot >= num_phys) continue;
+    const int64_t dst = (((int64_t)slot * hkv + kv) * 256 + (t & 255)) * d8 + c;
+    kp[dst] = kc[u];
+    vp[dst] = vc[u];
+  }
+}
+
+hipError_t launch_page_append(int hkv, int head_dim, int tokens, int num_phys,
+                              const void* k_chunk, const void* v_chunk, const int32_t* slots,
+                              void* k_pool, void* v_pool, hipStream_t s) {
+  const int d8 = head_dim / 8;
+  const int64_t n16 = (int64_t)hkv * tokens * d8;
+  if (n16 <= 0) return hipSuccess;
+  const int64_t want = (n16 + 255) / 256;
+  dim3 g((unsigned)(want < 8192 ? want : 8192)), b(256);
+  hipLaunchKernelGGL(k_page_append, g, b, 0, s, hkv, d8, tokens, n16, num_phys,
+                     static_cast<const uint4*>(k_chunk), static_cast<const uint4*>(v_chunk), slots,
+                     static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool));
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(int groups, int nper, int64_t rows, int head_dim, const float* po,
                         const float* pm, const float* pl, bool final, void* out_o, float* out_m,
                         float* out_l, hipStream_t s) {

@@ -1,6 +1,7 @@
 """Replay driver: the prompt's paged K/V with its device page table, and the
 calls that replay one response (forward, LSE merge, response-only backward)
-or a whole group of responses one after another.
+or a whole group of responses one after another, and the chunked capture
+that writes the prompt's pages in the first place.
 
 The group loop follows the pages' serial suffix replay: the shared prompt is
 captured once and each response branch is replayed, back-propagated and freed
@@ -44,6 +45,7 @@ class PromptCache:
         order, offs = B.ls_kv_page_table(self.num_pages, B.PAGE_SIZE, self.prompt_len, l2p_np,
                                          self.num_phys, self.num_splits, policy, block_pages, owner)
         dev = k_pool.device
+        self.l2p = l2p_np
         self.order = order
         self.split_offsets_host = np.ascontiguousarray(offs)  # kept alive: the table points at it
         self._l2p_dev = torch.from_numpy(np.ascontiguousarray(l2p_np)).to(dev)
@@ -174,3 +176,59 @@ def replay_group(cache: PromptCache, members: Iterable[Member], consume=None, sc
         out.append(consume(i, fwd, dq, dk, dv) if consume is not None else None)
         del fwd, dq, dk, dv
     return out
+
+
+@dataclass
+class CaptureResult:
+    cache: PromptCache   # the captured prompt: every page written, one page table
+    outputs: List        # per chunk: (o bf16 [Hq, Tc, d], lse fp32 [Hq, Tc]) or consume's value
+
+
+def capture_prefill(chunks: Iterable, k_pool: torch.Tensor, v_pool: torch.Tensor, slots,
+                    num_splits: int = 1, policy: int = B.LS_SPLIT_CONTIGUOUS,
+                    block_pages: int = 1, scale=None, consume=None, stream=None) -> CaptureResult:
+    """Capture of one full-attention layer of the shared prompt: a no-grad
+    prefill, chunk by chunk, that keeps only the layer's K/V, as compact pages
+    (DeepRead summary page, "Method"; LongStraw review page, section 2, items 1
+    and 2; 4096-token chunks, same page, section 3).
+
+    ``chunks`` yields ``(q [Hq, Tc, d], k [Hkv, Tc, d], v [Hkv, Tc, d])``, bf16
+    and contiguous, for consecutive spans of the prompt; every chunk but the
+    last is a whole number of 256-token pages.  ``slots`` (int32, one per page
+    of the whole prompt) names the pool slot of each logical page.  Chunk
+    ``[c0, c1)`` attends to the pages already captured (positions ``< c0``,
+    dealt to ``num_splits`` splits like any prompt) and causally to itself, as
+    the response block of one forward; its K/V pages are then appended.  The
+    chunk's attention output goes to ``consume(index, o, lse)`` when given
+    (and is released after it), else it is kept.  Returns the final
+    :class:`PromptCache` over the pools and the per-chunk results."""
+    slots_np = np.ascontiguousarray(
+        np.asarray(slots.cpu() if isinstance(slots, torch.Tensor) else slots, dtype=np.int32))
+    num_phys = int(k_pool.shape[0])
+    if slots_np.ndim != 1 or np.unique(slots_np).size != slots_np.size:
+        raise ValueError("slots must be a 1-D list of distinct pool slots")
+    if slots_np.size and (slots_np.min() < 0 or slots_np.max() >= num_phys):
+        raise ValueError("slots must lie in [0, num_phys_pages)")
+    dev = k_pool.device
+    slots_dev = torch.from_numpy(slots_np.copy()).to(dev)
+    outputs: List = []
+    c0 = 0
+    for i, (q, k, v) in enumerate(chunks):
+        if c0 % B.PAGE_SIZE:
+            raise ValueError("only the last chunk may end inside a page")
+        tc = int(k.shape[1])
+        p0, p1 = c0 // B.PAGE_SIZE, (c0 + tc + B.PAGE_SIZE - 1) // B.PAGE_SIZE
+        if p1 > slots_np.size:
+            raise ValueError(f"slots name {slots_np.size} pages; chunk {i} needs {p1}")
+        cache = PromptCache(k_pool, v_pool, c0, slots_np[:p0], num_splits, policy, block_pages)
+        fwd = replay_forward(cache, q, k, v, scale, stream)
+        B.ls_kv_page_append(k, v, slots_np[p0:p1], slots_dev[p0:p1], k_pool, v_pool, stream)
+        if consume is not None:
+            outputs.append(consume(i, fwd.o, fwd.lse))
+        else:
+            outputs.append((fwd.o, fwd.lse))
+        del fwd, cache
+        c0 += tc
+    npages = (c0 + B.PAGE_SIZE - 1) // B.PAGE_SIZE
+    cache = PromptCache(k_pool, v_pool, c0, slots_np[:npages], num_splits, policy, block_pages)
+    return CaptureResult(cache, outputs)

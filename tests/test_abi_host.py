@@ -11,6 +11,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import response_replay_attention_amd as rra
@@ -276,3 +277,40 @@ def test_members_reject_bad_counts_and_pointers():
     assert _fwd_members(_shape(head_dim=64), pt, [0, 32, 64]) == UNSUPPORTED
     assert _fwd_members(sh, pt, [0, 32, 64], q=FAKE + 2) == INVALID
     assert _fwd_members(sh, pt, [0, 32, 64], ws_bytes=0) == WORKSPACE
+
+
+# ---------------------------------------------------------------- page writer
+
+def _append(hkv=4, d=256, tokens=300, slots=(5, 2), num_phys=8, **ptrs):
+    p = dict(k=FAKE, v=FAKE, slots_dev=FAKE, k_pool=FAKE, v_pool=FAKE)
+    p.update(ptrs)
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    return rra.lib().ls_kv_page_append(hkv, d, tokens, p["k"], p["v"],
+                                       sl.ctypes.data if sl.size else None, p["slots_dev"],
+                                       p["k_pool"], p["v_pool"], num_phys, None)
+
+
+def test_page_append_rejects_bad_slots():
+    assert _append(slots=(5, 8)) == PAGE_RANGE        # past the pool
+    assert _append(slots=(-1, 2)) == PAGE_RANGE       # negative
+    assert _append(slots=(3, 3)) == PAGE_RANGE        # one slot for two pages
+    assert _append(tokens=256, slots=(7,), num_phys=7) == PAGE_RANGE
+
+
+def test_page_append_rejects_bad_args():
+    assert _append(tokens=0) == INVALID
+    assert _append(hkv=0) == INVALID
+    assert _append(num_phys=0) == INVALID
+    assert _append(d=64) == UNSUPPORTED
+    assert _append(slots=()) == INVALID                # no host slots
+    assert _append(slots_dev=0) == INVALID
+    assert _append(k=FAKE + 8) == INVALID              # misaligned chunk
+    assert _append(v_pool=0) == INVALID
+    assert _append(hkv=8, d=256, tokens=1 << 20, slots=tuple(range(4096)), num_phys=4096) == UNSUPPORTED
+
+
+def test_page_append_wrapper_checks_slot_count():
+    k = torch.zeros(2, 300, 128, dtype=torch.bfloat16)
+    pool = torch.zeros(4, 2, 256, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rra.ls_kv_page_append(k, k, [0], torch.zeros(1, dtype=torch.int32), pool, pool)
