@@ -32,7 +32,8 @@
  *   - All argument checks happen before any HIP call, so a call that returns
  *     an error has enqueued nothing.
  *   - Supported: head_dim in {128, 256}; page_size == 256; Hq % Hkv == 0;
- *     resp_len >= 1; prompt_len >= 0; Hq*resp_len*head_dim < 2^31.
+ *     resp_len >= 1; prompt_len >= 0; Hq*resp_len*head_dim < 2^31;
+ *     Hkv*kv_rows*head_dim < 2^31.
  */
 #ifndef LS_REPLAY_H
 #define LS_REPLAY_H
@@ -63,14 +64,32 @@ enum {
   LS_SPLIT_EXPLICIT = 2     /* logical page p -> split owner[p] */
 };
 
+/* Flags of ls_attn_shape.flags. */
+enum {
+  LS_ACCUMULATE_KV = 1  /* ls_replay_attn_bwd adds into dk_resp / dv_resp instead of writing */
+};
+
 /* Shape of one replay-attention call.
  *   num_q_heads  Hq;  num_kv_heads Hkv, Hq % Hkv == 0; query head h reads
  *                K/V head h / (Hq/Hkv) (contiguous GQA groups).
  *   head_dim     d in {128, 256}.
  *   page_size    prompt tokens per page; must be 256.
  *   prompt_len   P >= 0 prompt positions; all are visible to every response row.
- *   resp_len     R >= 1 response rows; row i sees response keys 0..i.
- *   scale        softmax scale applied to q.k (normally 1/sqrt(d)). */
+ *   resp_len     R >= 1 response rows; row i sees response keys 0..q_offset+i.
+ *   scale        softmax scale applied to q.k (normally 1/sqrt(d)).
+ *   q_offset     >= 0.  0 for a whole response.  Otherwise the R rows are the
+ *                response tokens q_offset .. q_offset+R-1, one token block of
+ *                a longer response replayed on its own (the pages replay a
+ *                response in four blocks, in reverse; LongStraw review page,
+ *                section 7 mind map, and the cortexa abstract): the response
+ *                keys are its first q_offset + R tokens.
+ *   kv_rows      rows per KV head of k_resp, v_resp, dk_resp and dv_resp
+ *                ([Hkv, kv_rows, d]); 0 means q_offset + R, else it must be
+ *                >= q_offset + R and rows past q_offset + R are neither read
+ *                nor written (so one buffer of the whole response serves
+ *                every block).
+ *   flags        0 or LS_ACCUMULATE_KV.
+ * Zero-initialising the last three fields gives the whole-response call. */
 typedef struct ls_attn_shape {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -79,6 +98,9 @@ typedef struct ls_attn_shape {
   int64_t prompt_len;
   int32_t resp_len;
   float scale;
+  int32_t q_offset;
+  int32_t kv_rows;
+  int32_t flags;
 } ls_attn_shape;
 
 /* Page table of one prompt, as built by ls_kv_page_table and copied to the
@@ -145,7 +167,8 @@ size_t ls_replay_attn_bwd_workspace(const ls_attn_shape* shape, const ls_page_ta
  * composition by global LSE over CP ranks).
  * For every row (h, i) (row index h*R + i) and every part c in [0, S]:
  *   parts c < S   cover the prompt pages of split c (all positions visible);
- *   part  c == S  covers the response keys j <= i (causal, diagonal included).
+ *   part  c == S  covers the response keys j <= q_offset + i (causal, diagonal
+ *                 included).
  *   x_j = scale * <q[h,i], k_j>;  part_m[c,row] = m, part_l[c,row] = sum_j exp(x_j - m),
  *   part_o[c,row,:] = sum_j exp(x_j - m) v_j / part_l[c,row].
  * m is a shift chosen by the kernel (within a few units of max_j x_j, never
@@ -153,7 +176,7 @@ size_t ls_replay_attn_bwd_workspace(const ls_attn_shape* shape, const ls_page_ta
  * the split's log-sum-exp.  An empty split gives m = -inf, l = 0, o = 0.
  *   q                 device bf16 [Hq, R, d]
  *   k_pool, v_pool    device bf16 [num_phys_pages, Hkv, page_size, d]
- *   k_resp, v_resp    device bf16 [Hkv, R, d]
+ *   k_resp, v_resp    device bf16 [Hkv, kv_rows, d] (rows < q_offset + R are read)
  *   part_o            device fp32 [S+1, Hq, R, d]
  *   part_m, part_l    device fp32 [S+1, Hq, R]
  *   workspace         device, >= ls_replay_attn_fwd_workspace() bytes (may be
@@ -182,7 +205,8 @@ ls_status ls_replay_attn_fwd(const ls_attn_shape* shape, const ls_page_table* pt
  *   member_offsets       host int32 [G+1]: 0 = offs[0] < offs[1] < ... < offs[G] = R
  *   member_offsets_dev   device copy of member_offsets (may be NULL when G == 1)
  * Other arguments, workspace and errors as ls_replay_attn_fwd; offsets that
- * are not strictly increasing from 0 to R give LS_ERR_INVALID_ARG. */
+ * are not strictly increasing from 0 to R, or a nonzero q_offset, give
+ * LS_ERR_INVALID_ARG. */
 ls_status ls_replay_attn_fwd_members(const ls_attn_shape* shape, const ls_page_table* pt,
                                      int32_t num_members, const int32_t* member_offsets,
                                      const int32_t* member_offsets_dev, const void* q,
@@ -242,15 +266,19 @@ ls_status ls_lse_merge(int32_t num_parts, int64_t rows, int32_t head_dim,
  *                    order, the response term last (this replaces the pages'
  *                    dQ all-reduce across CP ranks; LongStraw review page,
  *                    section 2: only the query gradient is all-reduced);
- *   dk_resp[kv,j,:] = scale * sum_{h in group kv} sum_{i >= j} dS_ij q[h,i,:]
- *   dv_resp[kv,j,:] =         sum_{h in group kv} sum_{i >= j} P_ij  dO[h,i,:]
+ *   dk_resp[kv,j,:] = scale * sum_{h in group kv} sum_{i : q_offset+i >= j} dS_ij q[h,i,:]
+ *   dv_resp[kv,j,:] =         sum_{h in group kv} sum_{i : q_offset+i >= j} P_ij  dO[h,i,:]
+ * for the response keys j < q_offset + R: the contribution of these R rows
+ * (all of dK_r, dV_r for a whole response).  With LS_ACCUMULATE_KV it is added
+ * to what dk_resp / dv_resp hold, so the blocks of a response replayed one
+ * after another sum to the whole response's gradient.
  * No gradient of the prompt K/V is formed (stopgrad; DeepRead summary,
  * "Method"), and the pools are never written.
  *   q, d_o, o      device bf16 [Hq, R, d] (o as written by ls_lse_merge)
  *   lse            device fp32 [Hq, R]
  *   k_pool, v_pool, k_resp, v_resp as in the forward
  *   dq             device fp32 [Hq, R, d]
- *   dk_resp, dv_resp device fp32 [Hkv, R, d]
+ *   dk_resp, dv_resp device fp32 [Hkv, kv_rows, d]; rows >= q_offset + R untouched
  *   workspace      device, >= ls_replay_attn_bwd_workspace() bytes.
  * Errors: LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP. */
 ls_status ls_replay_attn_bwd(const ls_attn_shape* shape, const ls_page_table* pt,

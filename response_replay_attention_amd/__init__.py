@@ -11,6 +11,7 @@ prompt's pages.
 from .binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    LS_ACCUMULATE_KV,
     LS_SPLIT_BLOCK_CYCLIC,
     LS_SPLIT_CONTIGUOUS,
     LS_SPLIT_EXPLICIT,
@@ -38,10 +39,12 @@ from .replay import (  # noqa: F401
     ForwardResult,
     Member,
     PromptCache,
+    block_bounds,
     capture_prefill,
     replay_backward,
     replay_forward,
     replay_group,
     replay_member,
+    replay_token_blocks,
     score_group,
 )

@@ -21,6 +21,7 @@ LS_OK = 0
 LS_SPLIT_CONTIGUOUS = 0
 LS_SPLIT_BLOCK_CYCLIC = 1
 LS_SPLIT_EXPLICIT = 2
+LS_ACCUMULATE_KV = 1
 PAGE_SIZE = 256
 
 # every symbol include/ls_replay.h declares
@@ -48,6 +49,9 @@ class AttnShape(ctypes.Structure):
         ("prompt_len", ctypes.c_int64),
         ("resp_len", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("q_offset", ctypes.c_int32),
+        ("kv_rows", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -124,8 +128,10 @@ def _stream(stream) -> int:
 
 
 def make_shape(hq: int, hkv: int, head_dim: int, prompt_len: int, resp_len: int,
-               scale: float, page_size: int = PAGE_SIZE) -> AttnShape:
-    return AttnShape(hq, hkv, head_dim, page_size, prompt_len, resp_len, scale)
+               scale: float, page_size: int = PAGE_SIZE, q_offset: int = 0, kv_rows: int = 0,
+               flags: int = 0) -> AttnShape:
+    return AttnShape(hq, hkv, head_dim, page_size, prompt_len, resp_len, scale, q_offset, kv_rows,
+                     flags)
 
 
 # ----------------------------------------------------------------- C calls

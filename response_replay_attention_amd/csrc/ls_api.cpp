@@ -74,6 +74,13 @@ ls_status check_shape(const ls_attn_shape* sh) {
   if (sh->page_size != kPage) return LS_ERR_UNSUPPORTED;
   const int64_t elems = (int64_t)sh->num_q_heads * sh->resp_len * sh->head_dim;
   if (elems >= (int64_t(1) << 31)) return LS_ERR_UNSUPPORTED;
+  if (sh->q_offset < 0 || sh->kv_rows < 0) return LS_ERR_INVALID_ARG;
+  if (sh->flags & ~LS_ACCUMULATE_KV) return LS_ERR_INVALID_ARG;
+  const int64_t rk = (int64_t)sh->q_offset + sh->resp_len;
+  if (sh->kv_rows != 0 && sh->kv_rows < rk) return LS_ERR_INVALID_ARG;
+  const int64_t kvr = sh->kv_rows != 0 ? sh->kv_rows : rk;
+  if ((int64_t)sh->num_kv_heads * kvr * sh->head_dim >= (int64_t(1) << 31)) return LS_ERR_UNSUPPORTED;
+  if ((int64_t)sh->num_q_heads * rk * sh->head_dim >= (int64_t(1) << 31)) return LS_ERR_UNSUPPORTED;
   return LS_OK;
 }
 
@@ -145,6 +152,10 @@ AttnArgs base_args(const ls_attn_shape& sh, const ls_page_table& pt, const void*
   a.hq = sh.num_q_heads;
   a.hkv = sh.num_kv_heads;
   a.R = sh.resp_len;
+  a.qoff = sh.q_offset;
+  a.RK = sh.q_offset + sh.resp_len;
+  a.kvr = sh.kv_rows != 0 ? sh.kv_rows : a.RK;
+  a.kv_accum = (sh.flags & LS_ACCUMULATE_KV) != 0;
   a.scale = sh.scale;
   a.s2 = sh.scale * 1.4426950408889634f;
   return a;
@@ -153,11 +164,12 @@ AttnArgs base_args(const ls_attn_shape& sh, const ls_page_table& pt, const void*
 // Workspace layouts (each piece 256-byte aligned):
 //   forward:  phys [num_pages] int32 | (chunks > 1) o, m, l partials per unit
 //   backward: phys [num_pages] int32 | D [rows] | dQ partials [units + 1]
-//             | response dV/dK partials per query head [2][g][Hkv][R][d]
+//             | response dV/dK partials per query head [2][g][Hkv][q_offset + R][d]
 size_t phys_bytes(const ls_page_table& pt) { return round_up((size_t)pt.num_pages * 4, 256); }
 
 size_t kv_part_bytes(const ls_attn_shape& sh) {
-  return round_up((size_t)2 * sh.num_q_heads * sh.resp_len * sh.head_dim * 4, 256);
+  return round_up((size_t)2 * sh.num_q_heads * ((size_t)sh.q_offset + sh.resp_len) * sh.head_dim * 4,
+                  256);
 }
 
 size_t fwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt) {
@@ -268,7 +280,7 @@ const char* ls_status_string(ls_status s) {
   return "unknown status";
 }
 
-int32_t ls_version(void) { return 100; }
+int32_t ls_version(void) { return 101; }
 
 ls_status ls_kv_page_table(int32_t num_pages, int32_t page_size, int64_t prompt_len,
                            const int32_t* l2p, int32_t num_phys_pages, int32_t num_splits,
@@ -346,6 +358,7 @@ ls_status ls_replay_attn_fwd_members(const ls_attn_shape* sh, const ls_page_tabl
                                      hipStream_t stream) {
   if (!sh || num_members < 1 || !member_offsets) return LS_ERR_INVALID_ARG;
   if (num_members > 1 && !member_offsets_dev) return LS_ERR_INVALID_ARG;
+  if (sh->q_offset != 0) return LS_ERR_INVALID_ARG;  // members are whole responses
   if (member_offsets[0] != 0 || member_offsets[num_members] != sh->resp_len)
     return LS_ERR_INVALID_ARG;
   for (int32_t k = 0; k < num_members; ++k)
@@ -461,9 +474,8 @@ ls_status ls_replay_attn_bwd(const ls_attn_shape* sh, const ls_page_table* pt, c
   st = run("bwd_resp_dkdv", stream, [&] { return launch_bwd_dkdv(r, d, stream); });
   if (st != LS_OK) return st;
   st = run("kv_reduce", stream, [&] {
-    return launch_kv_reduce(sh->num_q_heads / sh->num_kv_heads,
-                            (int64_t)sh->num_kv_heads * sh->resp_len * d, kv_part, dv_resp, dk_resp,
-                            stream);
+    return launch_kv_reduce(sh->num_q_heads / sh->num_kv_heads, sh->num_kv_heads, r.RK, r.kvr, d,
+                            r.kv_accum != 0, kv_part, dv_resp, dk_resp, stream);
   });
   if (st != LS_OK) return st;
   return run("dq_reduce", stream, [&] {

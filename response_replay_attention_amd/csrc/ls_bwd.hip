@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int key = crow(r, hf);
         bool ok = key < nv;
-        if (RESP) ok = ok && (key0 + key <= qi);
+        if (RESP) ok = ok && (key0 + key <= qi + a.qoff);
         x[r] = ok ? s[r] : -kInf;
       }
       bf16x8 dsb[2];
@@ -290,8 +290,9 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
 }
 
 // dK or dV of 32 response keys [j0, j0+32) of KV head kv from the query head
-// kv*g + blockIdx.z, one wave per workgroup, key-stationary: loops over every
-// query block i0 >= j0 of that head, accumulating
+// kv*g + blockIdx.z, one wave per workgroup, key-stationary: loops over the
+// query rows i of that head that see the keys (qoff + i >= j0, in blocks of
+// 32 from i = max(0, j0 - qoff)), accumulating
 //   DV:  dV^T[d][key] += sum_query dO[query][d] P[query][key]
 //   DK:  dK^T[d][key] += sum_query Q[query][d]  dS[query][key]
 // with S = Q K^T and dP = dO V^T recomputed in the (query x key) orientation.
@@ -317,9 +318,9 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
   uint16_t* qt = smem + 2 * TILE;
   uint16_t* dt = smem + 3 * TILE;
 
-  const int nkeys = min(kBN, a.R - j0);
+  const int nkeys = min(kBN, a.RK - j0);
   {
-    const size_t off = ((size_t)kv * a.R + j0) * D;
+    const size_t off = ((size_t)kv * a.kvr + j0) * D;
     tile_load_async<D, 1>(kt, a.k + off, nkeys, 0, lane);
     if (DK) tile_load_async<D, 1>(vt, a.v + off, nkeys, 0, lane);
   }
@@ -334,7 +335,7 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
 
   {
     const int h = kv * g + hh;
-    for (int i0 = j0; i0 < a.R; i0 += kBN) {
+    for (int i0 = max(0, j0 - a.qoff); i0 < a.R; i0 += kBN) {
       const int nq = min(kBN, a.R - i0);
       const size_t qoff = ((size_t)h * a.R + i0) * D;
       __syncthreads();  // previous block's reads of qt/dt and s_* are done
@@ -367,7 +368,7 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = crow(r, hf);
-        const bool ok = (q < nq) && (key < a.R) && (key <= i0 + q);
+        const bool ok = (q < nq) && (key < a.RK) && (key <= a.qoff + i0 + q);
         const float p = ok ? __builtin_amdgcn_exp2f(s[r] * a.s2 - s_lse2[q]) : 0.f;
         const float val = DK ? p * (dp[r] - s_dval[q]) : p;
         pb[r >> 3][r & 7] = to_bf16(val);
@@ -383,9 +384,9 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
     }
   }
 
-  if (key < a.R) {
+  if (key < a.RK) {
     const float mul = DK ? a.scale : 1.f;
-    float* op = a.kv_part + ((((size_t)(DK ? g : 0) + hh) * a.hkv + kv) * a.R + key) * D + 4 * hf;
+    float* op = a.kv_part + ((((size_t)(DK ? g : 0) + hh) * a.hkv + kv) * a.RK + key) * D + 4 * hf;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
@@ -415,7 +416,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, h
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s) {
-  dim3 g((a.R + kBN - 1) / kBN, a.hkv, a.hq / a.hkv), b(64);
+  dim3 g((a.RK + kBN - 1) / kBN, a.hkv, a.hq / a.hkv), b(64);
   if (head_dim == 256) {
     hipLaunchKernelGGL((k_bwd_resp_kv<256, false>), g, b, 0, s, a);
     hipLaunchKernelGGL((k_bwd_resp_kv<256, true>), g, b, 0, s, a);

@@ -334,12 +334,12 @@ struct KeyWalk {
       : a(args), kv(kv_), p0(0), nblocks(0), nfull(0), jfirst(0) {
     const int GR = (a.hq / a.hkv) * a.R;
     if (RESP) {
-      // keys [first key of the first row's member, last row] cover every row
-      // of the tile when it stays inside one query head; else all keys
+      // keys [first key of the first row's member, qoff + last row] cover
+      // every row of the tile when it stays inside one query head; else all
       const int mlast = min(m0 + rows, GR) - 1;
       const bool one_head = m0 / a.R == mlast / a.R;
       const int imax = one_head ? mlast % a.R : a.R - 1;
-      nblocks = (imax + kBN) / kBN;
+      nblocks = (a.qoff + imax + kBN) / kBN;
       jfirst = one_head ? member_start(a, m0 % a.R) / kBN : 0;
       nfull = 0;
     } else {
@@ -369,8 +369,8 @@ struct KeyWalk {
   __device__ __forceinline__ size_t block(int b, int& nvalid, int& key0) const {
     if (RESP) {
       key0 = b * kBN;
-      nvalid = min(kBN, a.R - key0);
-      return ((size_t)kv * a.R + key0) * D;
+      nvalid = min(kBN, a.RK - key0);
+      return ((size_t)kv * a.kvr + key0) * D;
     }
     key0 = 0;
     nvalid = 0;

@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
           const i32x4 none = {0, 0, 0, 0};
           fwd_step<D, true, false>(tl, ldr, k0, v0, qr, acc, a.s2, pass0 && mref == -kInf, mref,
                                    mlane, lsum, 0, none, 0, none, nv,
-                                   RESP ? qi - key0 : 0x7fffffff, hf,
+                                   RESP ? qi + a.qoff - key0 : 0x7fffffff, hf,
                                    RESP ? qlo - key0 : -0x7fffffff);
         }
         __syncthreads();  // tiles are rewritten by the next block

@@ -33,6 +33,10 @@ struct AttnArgs {
   int64_t prompt_len;
   int32_t num_pages, num_phys, chunks, chunk_pages;
   int32_t hq, hkv, R, mtiles;
+  // response keys: the rows are response tokens qoff .. qoff+R-1 and see keys
+  // j <= qoff + i; k/v (response) and dk/dv have kvr rows per KV head, of
+  // which the first RK = qoff + R are used; kv_accum: dk/dv += instead of =
+  int32_t qoff, RK, kvr, kv_accum;
   float s2;               // scale * log2(e)
   float scale;
   // forward outputs (slot arrays): o [slots, Hq*R, d], m/l [slots, Hq*R]
@@ -47,15 +51,16 @@ struct AttnArgs {
   float* dq_slots;        // fp32 [slots, Hq*R, d]
   float* dk;              // fp32 [Hkv, R, d]
   float* dv;
-  float* kv_part;         // fp32 [2][g][Hkv][R][d] per-query-head dV (0) / dK (1) partials
+  float* kv_part;         // fp32 [2][g][Hkv][RK][d] per-query-head dV (0) / dK (1) partials
 };
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s);
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s);
-// dv = sum_h kv_part[0][h], dk = sum_h kv_part[1][h] in head order
-hipError_t launch_kv_reduce(int g, int64_t elems, const float* part, float* dv, float* dk,
-                            hipStream_t s);
+// dv[kv][j] (=, or += when accum) sum_h kv_part[0][h][kv][j], dk likewise from
+// kv_part[1], heads in order; j < rk, output rows strided by kvr
+hipError_t launch_kv_reduce(int g, int hkv, int rk, int kvr, int head_dim, bool accum,
+                            const float* part, float* dv, float* dk, hipStream_t s);
 
 // Merge `nper` consecutive parts per group: group c reads parts
 // [c*nper, (c+1)*nper).  final=true writes bf16 O and natural-log LSE;

@@ -135,10 +135,15 @@ hipError_t launch_resolve_pages(int32_t num_pages, int32_t num_phys, const int32
 
 // dv = sum over the g query heads of part[0], dk = sum of part[1], in head
 // order (deterministic); part is [2][g][elems].
-__global__ void __launch_bounds__(256) k_kv_reduce(int g, int64_t n4, const float4* __restrict__ part,
+// Partials are [2][g][Hkv][rk][d]; element i of one [Hkv][rk][d] set goes to
+// output row (kv, j) of a [Hkv][kvr][d] tensor.
+__global__ void __launch_bounds__(256) k_kv_reduce(int g, int64_t n4, int64_t head4, int64_t ostride4,
+                                                   int accum, const float4* __restrict__ part,
                                                    float4* __restrict__ dv, float4* __restrict__ dk) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t kv = i / head4;
+    const int64_t o = kv * ostride4 + (i - kv * head4);
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       const float4* p = part + (size_t)w * g * n4 + i;
@@ -150,18 +155,28 @@ __global__ void __launch_bounds__(256) k_kv_reduce(int g, int64_t n4, const floa
         acc.z += v.z;
         acc.w += v.w;
       }
-      (w == 0 ? dv : dk)[i] = acc;
+      float4* out = (w == 0 ? dv : dk) + o;
+      if (accum) {
+        const float4 prev = *out;
+        acc.x = prev.x + acc.x;
+        acc.y = prev.y + acc.y;
+        acc.z = prev.z + acc.z;
+        acc.w = prev.w + acc.w;
+      }
+      *out = acc;
     }
   }
 }
 
-hipError_t launch_kv_reduce(int g, int64_t elems, const float* part, float* dv, float* dk,
-                            hipStream_t s) {
-  const int64_t n4 = elems / 4;
+hipError_t launch_kv_reduce(int g, int hkv, int rk, int kvr, int head_dim, bool accum,
+                            const float* part, float* dv, float* dk, hipStream_t s) {
+  const int64_t head4 = (int64_t)rk * head_dim / 4;
+  const int64_t n4 = hkv * head4;
   if (n4 <= 0) return hipSuccess;
   const int64_t want = (n4 + 255) / 256;
   dim3 gr((unsigned)(want < 4096 ? want : 4096)), b(256);
-  hipLaunchKernelGGL(k_kv_reduce, gr, b, 0, s, g, n4, reinterpret_cast<const float4*>(part),
+  hipLaunchKernelGGL(k_kv_reduce, gr, b, 0, s, g, n4, head4, (int64_t)kvr * head_dim / 4,
+                     accum ? 1 : 0, reinterpret_cast<const float4*>(part),
                      reinterpret_cast<float4*>(dv), reinterpret_cast<float4*>(dk));
   return hipGetLastError();
 }

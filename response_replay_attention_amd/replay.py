@@ -57,12 +57,14 @@ class PromptCache:
             self._offs_dev.data_ptr(), self.split_offsets_host.ctypes.data,
             self.num_pages, self.num_splits, self.num_phys)
 
-    def shape(self, q: torch.Tensor, scale: Optional[float] = None) -> B.AttnShape:
+    def shape(self, q: torch.Tensor, scale: Optional[float] = None, q_offset: int = 0,
+              kv_rows: int = 0, flags: int = 0) -> B.AttnShape:
         hq, r, d = q.shape
         if d != self.head_dim:
             raise ValueError("head_dim mismatch between q and the pools")
         s = 1.0 / math.sqrt(d) if scale is None else float(scale)
-        return B.make_shape(hq, self.hkv, d, self.prompt_len, r, s)
+        return B.make_shape(hq, self.hkv, d, self.prompt_len, r, s, q_offset=q_offset,
+                            kv_rows=kv_rows, flags=flags)
 
 
 @dataclass
@@ -74,10 +76,13 @@ class ForwardResult:
     part_l: torch.Tensor
 
 
-def replay_forward(cache: PromptCache, q, k_resp, v_resp, scale=None, stream=None) -> ForwardResult:
+def replay_forward(cache: PromptCache, q, k_resp, v_resp, scale=None, stream=None,
+                   q_offset: int = 0) -> ForwardResult:
     """Partial attention per split + the causal response block, then the exact
-    LSE merge."""
-    sh = cache.shape(q, scale)
+    LSE merge.  With ``q_offset`` the rows of ``q`` are response tokens
+    ``q_offset ..`` of a response whose K/V ``[Hkv, kv_rows, d]`` hold at least
+    its first ``q_offset + R`` tokens."""
+    sh = cache.shape(q, scale, q_offset, int(k_resp.shape[1]))
     hq, r, d = q.shape
     dev = q.device
     nparts = cache.num_splits + 1
@@ -128,15 +133,28 @@ def score_group(cache: PromptCache, members: Iterable["Member"], scale=None, str
     return [(o[:, offs[k]:offs[k + 1]], lse[:, offs[k]:offs[k + 1]]) for k in range(len(members))]
 
 
-def replay_backward(cache: PromptCache, q, k_resp, v_resp, o, lse, d_o, scale=None, stream=None):
+def replay_backward(cache: PromptCache, q, k_resp, v_resp, o, lse, d_o, scale=None, stream=None,
+                    q_offset: int = 0, dk=None, dv=None):
     """Response-only backward: returns ``(dq, dk_resp, dv_resp)`` in fp32.
-    The prompt pools get no gradient."""
-    sh = cache.shape(q, scale)
+    The prompt pools get no gradient.  ``dk``/``dv`` (fp32 ``[Hkv, kv_rows, d]``,
+    ``kv_rows`` = the rows of ``k_resp``), when given, receive the
+    contribution of these rows added to what they hold; otherwise fresh
+    tensors of ``k_resp``'s row count are returned, rows past
+    ``q_offset + R`` left zero."""
     hq, r, d = q.shape
+    kv_rows = int(k_resp.shape[1])
+    accumulate = dk is not None
+    if accumulate != (dv is not None):
+        raise ValueError("give both dk and dv, or neither")
+    sh = cache.shape(q, scale, q_offset, kv_rows, B.LS_ACCUMULATE_KV if accumulate else 0)
     dev = q.device
     dq = torch.empty(hq, r, d, dtype=torch.float32, device=dev)
-    dk = torch.empty(cache.hkv, r, d, dtype=torch.float32, device=dev)
-    dv = torch.empty(cache.hkv, r, d, dtype=torch.float32, device=dev)
+    if not accumulate:
+        dk = torch.empty(cache.hkv, kv_rows, d, dtype=torch.float32, device=dev)
+        dv = torch.empty(cache.hkv, kv_rows, d, dtype=torch.float32, device=dev)
+        if kv_rows > q_offset + r:
+            dk[:, q_offset + r:].zero_()
+            dv[:, q_offset + r:].zero_()
     wsb = B.ls_replay_attn_bwd_workspace(sh, cache.pt)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     B.ls_replay_attn_bwd(sh, cache.pt, q, cache.k_pool, cache.v_pool, k_resp, v_resp, o, lse, d_o,
@@ -232,3 +250,51 @@ def capture_prefill(chunks: Iterable, k_pool: torch.Tensor, v_pool: torch.Tensor
     npages = (c0 + B.PAGE_SIZE - 1) // B.PAGE_SIZE
     cache = PromptCache(k_pool, v_pool, c0, slots_np[:npages], num_splits, policy, block_pages)
     return CaptureResult(cache, outputs)
+
+
+def block_bounds(resp_len: int, blocks: int) -> List[tuple]:
+    """``blocks`` consecutive token blocks covering ``[0, resp_len)``, sizes
+    differing by at most one (longer first)."""
+    if blocks < 1 or blocks > resp_len:
+        raise ValueError("need 1 <= blocks <= resp_len")
+    base, extra = divmod(resp_len, blocks)
+    out, s = [], 0
+    for b in range(blocks):
+        e = s + base + (1 if b < extra else 0)
+        out.append((s, e))
+        s = e
+    return out
+
+
+def replay_token_blocks(cache: PromptCache, block_inputs: Iterable, k_resp, v_resp, scale=None,
+                        consume=None, stream=None):
+    """Reverse token-block replay of one response (the pages replay a response
+    in four blocks, in reverse: LongStraw review page, section 7 mind map;
+    read here as blocks of response tokens).  ``block_inputs`` lists, in
+    response order, ``(q_b [Hq, Rb, d], d_o_b [Hq, Rb, d])`` for consecutive
+    token blocks; ``k_resp``/``v_resp`` ``[Hkv, R, d]`` hold the whole
+    response.  Blocks are replayed last first: forward and merge of the
+    block's rows over the prompt and the response tokens up to each row, then
+    the backward, whose dK_r/dV_r contributions are added into one fp32
+    ``[Hkv, R, d]`` pair.  Each block's ``(index, fwd, dq)`` goes to
+    ``consume`` (if given) and is released before the next block.  Returns
+    ``(dk, dv, outputs)`` with ``outputs`` in response order."""
+    blocks = list(block_inputs)
+    hkv, R, d = (int(x) for x in k_resp.shape)
+    offs = [0]
+    for q_b, _ in blocks:
+        offs.append(offs[-1] + int(q_b.shape[1]))
+    if offs[-1] != R:
+        raise ValueError(f"blocks cover {offs[-1]} rows, the response has {R}")
+    dev = k_resp.device
+    dk = torch.zeros(hkv, R, d, dtype=torch.float32, device=dev)
+    dv = torch.zeros(hkv, R, d, dtype=torch.float32, device=dev)
+    outputs: List = [None] * len(blocks)
+    for b in reversed(range(len(blocks))):
+        q_b, d_o_b = blocks[b]
+        fwd = replay_forward(cache, q_b, k_resp, v_resp, scale, stream, q_offset=offs[b])
+        dq, _, _ = replay_backward(cache, q_b, k_resp, v_resp, fwd.o, fwd.lse, d_o_b, scale, stream,
+                                   q_offset=offs[b], dk=dk, dv=dv)
+        outputs[b] = consume(b, fwd, dq) if consume is not None else (fwd, dq)
+        del fwd, dq
+    return dk, dv, outputs

@@ -166,6 +166,12 @@ def _bwd(sh, pt, **ptrs):
     (dict(scale=float("nan")), INVALID),
     (dict(prompt_len=5 * 256), INVALID),   # table has 4 pages, prompt needs 5
     (dict(resp_len=1 << 20), UNSUPPORTED), # Hq*R*d >= 2^31
+    (dict(q_offset=-1), INVALID),
+    (dict(q_offset=10, kv_rows=73), INVALID),            # kv_rows < q_offset + R
+    (dict(kv_rows=-5), INVALID),
+    (dict(flags=2), INVALID),                            # unknown flag
+    (dict(q_offset=(1 << 21) - 64), UNSUPPORTED),        # Hkv*(q_offset+R)*d >= 2^31
+    (dict(kv_rows=1 << 21), UNSUPPORTED),
 ])
 def test_fwd_bwd_reject_bad_shapes(shape_kw, status):
     sh, pt = _shape(**shape_kw), _table()
@@ -314,3 +320,25 @@ def test_page_append_wrapper_checks_slot_count():
     pool = torch.zeros(4, 2, 256, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         rra.ls_kv_page_append(k, k, [0], torch.zeros(1, dtype=torch.int32), pool, pool)
+
+
+
+# ---------------------------------------------------------- token-block shape
+
+def test_token_block_shape_accepted_and_sized():
+    """q_offset / kv_rows pass validation (the calls then stop at the missing
+    workspace, before any HIP call) and size the response dK/dV partials."""
+    pt = _table()
+    whole = _shape()
+    block = _shape(q_offset=192, kv_rows=512)
+    assert _fwd(block, pt, ws_bytes=0) == WORKSPACE
+    assert _bwd(block, pt, ws_bytes=0) == WORKSPACE
+    assert _bwd(_shape(flags=B.LS_ACCUMULATE_KV), pt, ws_bytes=0) == WORKSPACE
+    grow = rra.ls_replay_attn_bwd_workspace(block, pt) - rra.ls_replay_attn_bwd_workspace(whole, pt)
+    # [2][Hq][q_offset + R][d] fp32 partials: 192 more keys
+    assert grow == 2 * 24 * 192 * 256 * 4
+    assert rra.ls_replay_attn_fwd_workspace(block, pt) == rra.ls_replay_attn_fwd_workspace(whole, pt)
+
+
+def test_members_reject_q_offset():
+    assert _fwd_members(_shape(q_offset=32), _table(), [0, 32, 64]) == INVALID
