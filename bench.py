@@ -14,6 +14,9 @@ eight members (R = 512 ... 4096) over the shared prompt, `prompt_keys_per_s` cou
 times members, and the line also carries each member's time from one extra, untimed pass.
 ``--score`` times forward-only scoring instead: all members in one pass over the prompt
 (``ls_replay_attn_fwd_members``) and the merge, counting forward flops only.
+``--blocks N`` replays the member as N token blocks, last block first (each block's forward,
+merge and backward at its offset in the response, dK/dV added into one buffer); the flops are
+those of the whole member.
 A name in ``replay_inputs.CAPTURE_WORKLOADS`` times the chunked capture of one full-attention
 layer instead: a step prefills the whole prompt chunk by chunk (each chunk's forward over the
 pages before it and itself, the merge, and the append of its pages); flops are the forward's.
@@ -284,6 +287,8 @@ def main() -> int:
     ap.add_argument("--score", action="store_true",
                     help="forward-only scoring of all members in one pass over the prompt "
                          "(merged O and LSE per member, no backward)")
+    ap.add_argument("--blocks", type=int, default=1,
+                    help="replay the member as this many token blocks, last block first")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -300,9 +305,10 @@ def main() -> int:
                                make_inputs, make_response)
     if args.workload in CAPTURE_WORKLOADS:
         return bench_capture(args, CAPTURE_WORKLOADS[args.workload])
-    from response_replay_attention_amd import (Member, PromptCache, ls_timing_enable,
+    from response_replay_attention_amd import (Member, PromptCache, block_bounds, ls_timing_enable,
                                                ls_timing_read, ls_timing_reset, replay_backward,
-                                               replay_forward, replay_group, score_group)
+                                               replay_forward, replay_group, replay_token_blocks,
+                                               score_group)
 
     shape = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -316,6 +322,12 @@ def main() -> int:
     for i, sh in enumerate(member_shapes[1:], start=1):
         r = make_response(sh, args.seed + i, device=dev)
         members.append(Member(r["q"], r["k_resp"], r["v_resp"], r["d_o"]))
+    if args.blocks > 1 and (group or args.score):
+        print("--blocks applies to one member's replay", file=sys.stderr)
+        return 2
+    m0 = members[0]
+    bounds = block_bounds(shape.resp_len, args.blocks) if args.blocks > 1 else []
+    block_inputs = [(m0.q[:, s:e].contiguous(), m0.d_o[:, s:e].contiguous()) for s, e in bounds]
     torch.cuda.synchronize()
 
     def make_cache():
@@ -329,6 +341,10 @@ def main() -> int:
             return
         if group:
             replay_group(cache, members, scale=shape.scale)
+            return
+        if block_inputs:
+            replay_token_blocks(cache, block_inputs, m0.k_resp, m0.v_resp, shape.scale,
+                                consume=lambda b, fwd, dq: None)
             return
         m = members[0]
         fwd = replay_forward(cache, m.q, m.k_resp, m.v_resp, shape.scale)
@@ -372,6 +388,8 @@ def main() -> int:
     dom_flops = sum(f["fwd_prompt" if args.score else "bwd_prompt_dq"] for f in per_member)
     if not args.score:
         dom_flops /= len(per_member)
+    if block_inputs:  # one dominant launch per block, each over its own rows
+        dom_flops /= len(block_inputs)
     achieved = dom_flops / (dom["avg_ms"] * 1e-3) / 1e12
     digest = source_digest()
     traffic = None if args.score else read_traffic(digest)
@@ -410,6 +428,10 @@ def main() -> int:
         },
         "kernels_avg_ms": {k: round(v["avg_ms"], 4) for k, v in kern.items()},
     }
+    if block_inputs:
+        out["config"]["token_blocks"] = [list(b) for b in bounds]
+        out["config"]["mode"] = "reverse token-block replay"
+        out["roofline"]["traffic"] = None
     if args.score:
         out["metric"] = "group scoring (forward only) TFLOP/s & prompt-keys/s; % bf16 MFMA peak"
         out["config"]["mode"] = "score"
