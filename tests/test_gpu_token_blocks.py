@@ -9,7 +9,9 @@ response (q_offset), against the float64 oracle of the whole response.
   contribution of exactly that block's rows, and LS_ACCUMULATE_KV adds that
   contribution to what the buffers held;
 * blocks that do not start on a 32-row tile, a block of one row, and no
-  prompt.
+  prompt;
+* the 2,097,152-position prefix in four blocks with Q = 0, against the closed
+  form of every row's O and LSE and of the summed dV_r (dK_r must be 0).
 """
 import numpy as np
 import pytest
@@ -114,3 +116,34 @@ def test_one_block_contribution_and_untouched_rows():
     assert_close("dK_r accumulated", dk2[:, :e], bk[:, :e] + dk_r[:, :e])
     assert_close("dV_r accumulated", dv2[:, :e], bv[:, :e] + dv_r[:, :e])
     assert torch.equal(dk2[:, e:], base_k[:, e:]) and torch.equal(dv2[:, e:], base_v[:, e:])
+
+
+def test_token_blocks_zero_query_full_size():
+    """The 2,097,152-position prefix, R = 1024 as four blocks replayed in
+    reverse, Q = 0: every visible key has weight 1/n_i with n_i = P + i + 1
+    (i = the row's index in the whole response), so for every row of every
+    block LSE = ln n_i and O = (sum of visible values) / n_i; dK_r = 0 exactly
+    (every term carries a factor of q), and dV_r[j] = sum over heads h of the
+    group and rows i >= j of dO[h, i] / n_i, summed over the blocks."""
+    from replay_inputs import FULL_2M
+    shape = FULL_2M
+    P, R, g = shape.prompt_len, shape.resp_len, shape.hq // shape.hkv
+    print(f"case {shape.name} 4 token blocks, Q=0", flush=True)
+    inp = make_inputs(shape, seed=20260044, device="cuda", q_zero=True)
+    bounds = block_bounds(R, 4)
+    blocks = [(inp["q"][:, s:e].contiguous(), inp["d_o"][:, s:e].contiguous()) for s, e in bounds]
+    dk, dv, outs = replay_token_blocks(_cache(shape, inp), blocks, inp["k_resp"], inp["v_resp"],
+                                       shape.scale, consume=lambda b, fwd, dq: (fwd.o, fwd.lse))
+    torch.cuda.synchronize()
+    n = torch.arange(R, device="cuda", dtype=torch.float64) + P + 1
+    for kv in range(shape.hkv):
+        psum = logical_prompt(inp["v_pool"], inp["l2p"], P, kv_heads=[kv])[0].double().sum(0)
+        want_o = (psum[None, :] + torch.cumsum(inp["v_resp"][kv].double(), 0)) / n[:, None]
+        for (s, e), (o, lse) in zip(bounds, outs):
+            for h in range(kv * g, (kv + 1) * g):
+                assert_lse_close(f"LSE [{s},{e}) h{h}", lse[h], torch.log(n[s:e]).cpu().numpy())
+                assert_close(f"O [{s},{e}) h{h}", o[h], want_o[s:e].cpu().numpy())
+        w = (inp["d_o"][kv * g:(kv + 1) * g].double() / n[None, :, None]).sum(0)   # [R, d]
+        want_dv = torch.flip(torch.cumsum(torch.flip(w, [0]), 0), [0])             # sum over i >= j
+        assert_close(f"dV_r kv{kv}", dv[kv], want_dv.cpu().numpy())
+    assert bool((dk == 0).all()), "dK_r must vanish when Q = 0"
