@@ -103,8 +103,9 @@ def cpu_baseline(shape, inp, seconds_hint: float = 20.0):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     g = shape.hq // shape.hkv
-    # about 20 s of host work: ~2e6 (row x prompt-key) pairs per second measured
-    rows = max(1, min(16, shape.resp_len, (8 << 20) // max(shape.prompt_len, 1)))
+    # about 15 s of host work at the 2M prefix: ~1.2e7 (row x prompt-key)
+    # pairs per second measured for forward + backward
+    rows = max(1, min(64, shape.resp_len, (32 << 20) // max(shape.prompt_len, 1)))
     t0 = time.perf_counter()
     kp = logical_prompt(inp["k_pool"], inp["l2p"], shape.prompt_len, kv_heads=[0]).cpu()
     vp = logical_prompt(inp["v_pool"], inp["l2p"], shape.prompt_len, kv_heads=[0]).cpu()
