@@ -290,6 +290,8 @@ def main() -> int:
                          "(merged O and LSE per member, no backward)")
     ap.add_argument("--blocks", type=int, default=1,
                     help="replay the member as this many token blocks, last block first")
+    ap.add_argument("--identity-pages", action="store_true",
+                    help="place logical page p in pool slot p instead of a seeded random slot")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -318,7 +320,7 @@ def main() -> int:
     # the group replays G members of different lengths over one shared prompt;
     # every other workload is one member
     member_shapes = ([shape.with_(resp_len=r) for r in GROUP_2M_RESP_LENS] if group else [shape])
-    inp = make_inputs(member_shapes[0], args.seed, device=dev)
+    inp = make_inputs(member_shapes[0], args.seed, device=dev, identity_pages=args.identity_pages)
     members = [Member(inp["q"], inp["k_resp"], inp["v_resp"], inp["d_o"])]
     for i, sh in enumerate(member_shapes[1:], start=1):
         r = make_response(sh, args.seed + i, device=dev)
@@ -429,6 +431,8 @@ def main() -> int:
         },
         "kernels_avg_ms": {k: round(v["avg_ms"], 4) for k, v in kern.items()},
     }
+    if args.identity_pages:
+        out["config"]["page_layout"] = "identity"
     if block_inputs:
         out["config"]["token_blocks"] = [list(b) for b in bounds]
         out["config"]["mode"] = "reverse token-block replay"
