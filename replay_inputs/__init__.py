@@ -127,7 +127,9 @@ class CaptureShape:
 
 CAPTURE_256K = CaptureShape("capture_24x4_d256_p262144_c4096_s8", 24, 4, 256, 262_144, 4096, 8,
                             SPLIT_BLOCK_CYCLIC, 1)
-CAPTURE_WORKLOADS = {CAPTURE_256K.name: CAPTURE_256K}
+CAPTURE_2M = CaptureShape("capture_24x4_d256_p2097152_c4096_s8", 24, 4, 256, 2_097_152, 4096, 8,
+                          SPLIT_BLOCK_CYCLIC, 1)
+CAPTURE_WORKLOADS = {c.name: c for c in (CAPTURE_256K, CAPTURE_2M)}
 
 
 def make_capture_inputs(shape: CaptureShape, seed: int, device="cpu") -> Dict[str, object]:
