@@ -12,6 +12,9 @@ the arithmetic runs in libls_replay.so.
 """
 from __future__ import annotations
 
+import contextlib
+import functools
+import inspect
 import math
 from dataclasses import dataclass
 from typing import Iterable, List, Optional
@@ -20,6 +23,28 @@ import numpy as np
 import torch
 
 from . import binding as B
+
+
+def _on_stream(fn):
+    """Run a driver with ``stream`` (a ``torch.cuda.Stream``, a raw handle or
+    None for the current stream) as torch's current stream, so that every
+    buffer the driver allocates belongs to the stream its kernels run on and
+    the caching allocator never hands it to other work while they may still
+    read it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapped(*args, **kw):
+        stream = sig.bind_partial(*args, **kw).arguments.get("stream")
+        if stream is None:
+            ctx = contextlib.nullcontext()
+        elif isinstance(stream, int):
+            ctx = torch.cuda.stream(torch.cuda.ExternalStream(stream))
+        else:
+            ctx = torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, **kw)
+    return wrapped
 
 
 class PromptCache:
@@ -76,6 +101,7 @@ class ForwardResult:
     part_l: torch.Tensor
 
 
+@_on_stream
 def replay_forward(cache: PromptCache, q, k_resp, v_resp, scale=None, stream=None,
                    q_offset: int = 0) -> ForwardResult:
     """Partial attention per split + the causal response block, then the exact
@@ -100,6 +126,7 @@ def replay_forward(cache: PromptCache, q, k_resp, v_resp, scale=None, stream=Non
     return ForwardResult(o, lse, part_o, part_m, part_l)
 
 
+@_on_stream
 def score_group(cache: PromptCache, members: Iterable["Member"], scale=None, stream=None) -> List:
     """Forward-only scoring of a whole group in one pass over the prompt: the
     members' queries and response K/V are stacked along the response axis, the
@@ -133,6 +160,7 @@ def score_group(cache: PromptCache, members: Iterable["Member"], scale=None, str
     return [(o[:, offs[k]:offs[k + 1]], lse[:, offs[k]:offs[k + 1]]) for k in range(len(members))]
 
 
+@_on_stream
 def replay_backward(cache: PromptCache, q, k_resp, v_resp, o, lse, d_o, scale=None, stream=None,
                     q_offset: int = 0, dk=None, dv=None):
     """Response-only backward: returns ``(dq, dk_resp, dv_resp)`` in fp32.
@@ -173,6 +201,7 @@ class Member:
     d_o: torch.Tensor
 
 
+@_on_stream
 def replay_member(cache: PromptCache, m: Member, scale=None, stream=None):
     """Forward, merge and backward of one member.  Returns
     ``(ForwardResult, dq, dk_resp, dv_resp)``."""
@@ -181,6 +210,7 @@ def replay_member(cache: PromptCache, m: Member, scale=None, stream=None):
     return fwd, dq, dk, dv
 
 
+@_on_stream
 def replay_group(cache: PromptCache, members: Iterable[Member], consume=None, scale=None,
                  stream=None) -> List:
     """Serial replay of a group against one shared prompt.  Each member's
@@ -202,6 +232,7 @@ class CaptureResult:
     outputs: List        # per chunk: (o bf16 [Hq, Tc, d], lse fp32 [Hq, Tc]) or consume's value
 
 
+@_on_stream
 def capture_prefill(chunks: Iterable, k_pool: torch.Tensor, v_pool: torch.Tensor, slots,
                     num_splits: int = 1, policy: int = B.LS_SPLIT_CONTIGUOUS,
                     block_pages: int = 1, scale=None, consume=None, stream=None) -> CaptureResult:
@@ -266,6 +297,7 @@ def block_bounds(resp_len: int, blocks: int) -> List[tuple]:
     return out
 
 
+@_on_stream
 def replay_token_blocks(cache: PromptCache, block_inputs: Iterable, k_resp, v_resp, scale=None,
                         consume=None, stream=None):
     """Reverse token-block replay of one response (the pages replay a response

@@ -217,3 +217,25 @@ def test_no_prompt_gradient_output_exists():
     cache, fwd, dq, dk, dv = run_hip(shape, inp)
     assert dq.shape == inp["q"].shape
     assert dk.shape == dv.shape == inp["k_resp"].shape
+
+
+def test_side_stream_gives_the_same_bits():
+    """The drivers on a side stream (torch.cuda.Stream, default priority) and
+    as a raw handle give bit-identical results to the current stream."""
+    shape = SMALL[1]
+    print(f"case {shape.name} side stream", flush=True)
+    inp = make_inputs(shape, seed=12, device="cuda")
+    cache = PromptCache(inp["k_pool"], inp["v_pool"], shape.prompt_len, inp["l2p"],
+                        shape.num_splits, shape.policy, shape.block_pages)
+    args = (inp["q"], inp["k_resp"], inp["v_resp"])
+    ref = replay_forward(cache, *args, shape.scale)
+    ref_g = replay_backward(cache, *args, ref.o, ref.lse, inp["d_o"], shape.scale)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for st in (side, side.cuda_stream):
+        fwd = replay_forward(cache, *args, shape.scale, stream=st)
+        g = replay_backward(cache, *args, fwd.o, fwd.lse, inp["d_o"], shape.scale, stream=st)
+        side.synchronize()
+        assert torch.equal(fwd.o, ref.o) and torch.equal(fwd.lse, ref.lse)
+        for a, b in zip(g, ref_g):
+            assert torch.equal(a, b)
