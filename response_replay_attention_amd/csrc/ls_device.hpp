@@ -168,6 +168,45 @@ struct LanesX {
   }
 };
 
+// Forward tiles in chunk-major layouts.  K keeps the 16-byte chunk c (elements
+// [8c, 8c+8)) of key row r in 16-byte slot c*32 + r; V keeps chunk C of row r
+// in slot C*32 + (r ^ 4*(C & 3)).  With these, every operand read is one
+// per-lane base register plus an immediate, so no address arithmetic sits
+// between an MFMA and the read it waits for:
+//   K row read, k-step kk:            kb + 1024*kk bytes
+//   V transposed read (ks, mt, half): vb[half] + 2048*mt + 256*ks bytes
+// and both are free of LDS bank conflicts for their own read pattern (64 banks
+// of 4 bytes; checked on the CPU for every lane and read, together with the
+// copies, at d = 128 and 256).  The registers the reads fill are the same as
+// with the row-major swizzled tiles (row8 / col8 above).
+template <int D>
+struct LanesCM {
+  int kb, vb0, vb1;  // byte offsets inside a tile
+  __device__ __forceinline__ LanesCM(int hf, int lq) {
+    kb = 512 * hf + 16 * lq;
+    const int L = lq & 15, g1 = lq >> 4, q = 2 * g1 + ((L >> 1) & 1);
+    vb0 = 512 * q + 16 * ((4 * hf + (L >> 2)) ^ (4 * q)) + 8 * (L & 1);
+    vb1 = 512 * q + 16 * ((8 + 4 * hf + (L >> 2)) ^ (4 * q)) + 8 * (L & 1);
+  }
+  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(kb), "+v"(vb0), "+v"(vb1)); }
+  __device__ __forceinline__ bf16x8 row8(const uint16_t* tile, int kk) const {
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(tile) + kb + 1024 * kk));
+  }
+  __device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int ks, int mt) const {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const char* base = reinterpret_cast<const char*>(tile) + 2048 * mt + 256 * ks;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + vb0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + vb1));
+    const s16x4 v[2] = {lo, hi};
+    u16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = (unsigned short)v[t >> 2][t & 3];
+    return __builtin_bit_cast(bf16x8, r);
+  }
+};
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Asynchronous copies of [32][D] bf16 blocks (row stride D) into LDS tiles,
@@ -295,6 +334,46 @@ __device__ __forceinline__ void load_block(const BlockLoader<D, NW>& L, uint16_t
   const uint32_t base = lds_addr(tile) + L.lds0;
 #pragma unroll
   for (int j = 0; j < BlockLoader<D, NW>::NIW; ++j) copy16_to_lds(base + j * 1024, L.voff[j], desc);
+}
+
+// Copies of [32][D] bf16 blocks into the chunk-major tiles of LanesCM, spread
+// over NW waves: copy instruction j of wave w fills slots (w*NIW + j)*64 + lane,
+// so lane (hl = lane / 32) reads the 16 bytes of chunk c = 2*(w*NIW + j) + hl of
+// row lane % 32 (K; V: of row (lane % 32) ^ 4*(c & 3)).  The source offsets of
+// copy 0 are kept; copy j adds 32*j bytes (the next chunk pair), and for V an
+// odd j also flips row bit 3 (c & 3 differs by 2).
+template <int D, int NW>
+struct BlockLoaderCM {
+  static constexpr int NIW = (kBN * D * 2 / 1024) / NW;  // wave instructions per block
+  static_assert(NIW * NW * 1024 == kBN * D * 2 && NIW <= 2, "tile must split evenly over the waves");
+  int vk, vv;  // byte offset of this lane's 16 bytes in the source block, copy 0 of K and of V
+  int lds0;    // byte offset of this wave's first 1 KB piece inside a tile (uniform)
+  __device__ __forceinline__ BlockLoaderCM(int wave, int lane)
+      : lds0(__builtin_amdgcn_readfirstlane(wave) * NIW * 1024) {
+    const int hl = lane >> 5;
+    vk = (lane & 31) * 2 * D + 16 * hl + 32 * wave * NIW;
+    vv = vk ^ (8 * D * ((wave * NIW * 2 + hl) & 3));
+  }
+  __device__ __forceinline__ int koff(int j) const { return vk + 32 * j; }
+  __device__ __forceinline__ int voff(int j) const { return ((j & 1) ? (vv ^ (16 * D)) : vv) + 32 * j; }
+  // copy instruction c of a step: K pieces first, then V
+  __device__ __forceinline__ void issue(int c, uint32_t kdst, i32x4 kdesc, uint32_t vdst,
+                                        i32x4 vdesc) const {
+    if (c < NIW) copy16_to_lds(kdst + lds0 + c * 1024, koff(c), kdesc);
+    else copy16_to_lds(vdst + lds0 + (c - NIW) * 1024, voff(c - NIW), vdesc);
+  }
+};
+
+// Rows [0, nvalid) of the block at `src` into a chunk-major tile (K or V
+// layout); bytes past the valid rows arrive as zeros.
+template <bool V, int D, int NW>
+__device__ __forceinline__ void load_block_cm(const BlockLoaderCM<D, NW>& L, uint16_t* tile,
+                                              const uint16_t* src, int nvalid) {
+  const i32x4 desc = block_desc(src, (unsigned)(nvalid * D * 2));
+  const uint32_t base = lds_addr(tile) + L.lds0;
+#pragma unroll
+  for (int j = 0; j < BlockLoaderCM<D, NW>::NIW; ++j)
+    copy16_to_lds(base + j * 1024, V ? L.voff(j) : L.koff(j), desc);
 }
 
 // Page-table entries are read through the constant address space: the tables

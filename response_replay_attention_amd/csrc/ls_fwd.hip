@@ -7,20 +7,22 @@
 // them (LongStraw review page, section 7 mind map, "Qwen3.6-27B
 // implementation": forward composition through a global LSE).
 //
-// gfx950 mapping (per workgroup: 4 waves, 128 query rows of one KV-head group):
+// gfx950 mapping (per workgroup: 8 waves, two per SIMD, 256 query rows of one
+// KV-head group):
 //   * the query heads of a KV group are packed into the M dimension, so every
-//     K/V byte staged in LDS serves 128 query rows;
+//     K/V byte staged in LDS serves 256 query rows;
 //   * each wave owns 32 query rows; its Q stays in registers as the B operand;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows read from LDS) puts
 //     one query per lane and 16 of the block's 32 keys per lane in registers,
 //     so the softmax statistics need one exchange between lanes l and l^32;
 //   * P^T (bf16) is the B operand of O^T = V^T P^T straight from registers; the
-//     V^T operand comes from the row-major V tile by transpose reads; O^T keeps
-//     one query per lane, so the shift and the final 1/l are per-lane scalars;
+//     V^T operand comes from the V tile by transpose reads; O^T keeps one query
+//     per lane, so the shift and the final 1/l are per-lane scalars;
+//   * K and V tiles are stored chunk-major (LanesCM), so each operand read is
+//     a base register plus an immediate offset;
 //   * full prompt blocks stream through a 4-stage LDS ring filled by
-//     buffer->LDS copies issued three blocks ahead, and the loop is software
-//     pipelined: the softmax of block b runs on the VALU while the MFMAs
-//     compute the scores of block b+1.  Masked blocks (the partial last prompt
+//     buffer->LDS copies issued three blocks ahead; the second wave on each
+//     SIMD covers one wave's waits.  Masked blocks (the partial last prompt
 //     page, the causal response block) take a simple loop of their own;
 //   * the exp2 shift is fixed at the first block's max instead of following
 //     the running max, so no accumulator is ever rescaled; an input whose
@@ -29,57 +31,6 @@
 #include "ls_device.hpp"
 
 namespace ls {
-
-// S^T[key][query] = sum_d K[key][d] Q[query][d] for the block in tile kt.
-template <int D>
-__device__ __forceinline__ f32x16 block_scores(const LanesX<D>& tl, const uint16_t* kt,
-                                               const bf16x8 (&qr)[D / 16]) {
-  f32x16 s;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) s = mfma32(tl.row8(kt, kk), qr[kk], s);
-  return s;
-}
-
-// Softmax numerators of one block for this lane's query: x = raw scores
-// (masked ones -inf), returns P^T as two bf16 B operands (register 8*ks + e
-// is k-element e of k-step ks), adds their fp32 sum to lsum.  Pass 0 fixes the
-// shift at the first block's max and flags scores that exceed it by more than
-// 2^kShiftSlack.
-__device__ __forceinline__ void block_probs(const float (&x)[16], float s2, bool pass0,
-                                            float& mref, float& mtrue, float& lsum,
-                                            bool& unsafe, bf16x8 (&pb)[2]) {
-  float mx = x[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-  const float mb = wave_max_halves(mx) * s2;
-  mtrue = fmaxf(mtrue, mb);
-  if (pass0) {
-    mref = (mref == -kInf) ? mb : mref;
-    unsafe = unsafe || (mb > mref + kShiftSlack);
-  }
-  const float mu = (mref == -kInf) ? 0.f : mref;
-  float ls = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], s2, -mu));
-    ls += p;
-    pb[r >> 3][r & 7] = to_bf16(p);
-  }
-  lsum += ls;
-}
-
-// O^T[d][query] += sum_key V[key][d] P^T[key][query] for the block in tile vt.
-template <int D>
-__device__ __forceinline__ void block_pv(f32x16 (&acc)[D / 32], const LanesX<D>& tl,
-                                         const uint16_t* vt, const bf16x8 (&pb)[2]) {
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma32(tl.col8(vt, ks, mt), pb[ks], acc[mt]);
-  }
-}
 
 // One step over a full key block b: S(b) = K(b) Q^T, P(b) = exp2(S s log2e -
 // mu) on the VALU, O^T += V(b)^T P(b), and the copies of block b+3.  Two
@@ -97,7 +48,7 @@ __device__ __forceinline__ void block_pv(f32x16 (&acc)[D / 32], const LanesX<D>&
 // after kmax (block-relative: the row's member start and its own position)
 // are masked; COPY: issue the block copies.
 template <int D, bool MASK, bool COPY>
-__device__ __forceinline__ void fwd_step(const LanesX<D>& tl, const BlockLoader<D, kFwdWaves>& ldr,
+__device__ __forceinline__ void fwd_step(const LanesCM<D>& tl, const BlockLoaderCM<D, kFwdWaves>& ldr,
                                          const uint16_t* kt, const uint16_t* vt,
                                          const bf16x8 (&qr)[D / 16], f32x16 (&acc)[D / 32],
                                          float s2, bool first, float& mu, float& mlane,
@@ -107,7 +58,7 @@ __device__ __forceinline__ void fwd_step(const LanesX<D>& tl, const BlockLoader<
   constexpr int NS = D / 16;   // score MFMAs per step = PV MFMAs per step
   constexpr int NMT = D / 32;  // 32-wide d tiles of O^T
   constexpr int PF = 1;        // LDS prefetch distance, in MFMAs
-  constexpr int NIW = BlockLoader<D, kFwdWaves>::NIW;
+  constexpr int NIW = BlockLoaderCM<D, kFwdWaves>::NIW;
   constexpr int CEV = NS / (2 * NIW);  // PV segments per copy instruction
   static_assert(CEV * 2 * NIW == NS, "copy instructions spread evenly over the PV MFMAs");
   bf16x8 kf[NS], vf[NS];
@@ -163,11 +114,7 @@ __device__ __forceinline__ void fwd_step(const LanesX<D>& tl, const BlockLoader<
   for (int j = 0; j < NS; ++j) {
     acc[j % NMT] = mfma32(vf[j], pb[j / NMT], acc[j % NMT]);
     if (j + PF < NS) vf[j + PF] = tl.col8(vt, (j + PF) / NMT, (j + PF) % NMT);
-    if (COPY && j % CEV == 0) {
-      const int c = j / CEV;
-      if (c < NIW) copy16_to_lds(kdst + ldr.lds0 + c * 1024, ldr.voff[c], kdesc);
-      else copy16_to_lds(vdst + ldr.lds0 + (c - NIW) * 1024, ldr.voff[c - NIW], vdesc);
-    }
+    if (COPY && j % CEV == 0) ldr.issue(j / CEV, kdst, kdesc, vdst, vdesc);
     __builtin_amdgcn_sched_barrier(0);
   }
   mlane = mx;
@@ -179,7 +126,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   constexpr int NMT = D / 32;
   constexpr int TILE = kBN * D;                     // elements of one K or V block
   constexpr int NST = kStages;                      // ring depth (4)
-  constexpr int NLD = 2 * BlockLoader<D, kFwdWaves>::NIW;  // copy instructions per wave per block
+  constexpr int NLD = 2 * BlockLoaderCM<D, kFwdWaves>::NIW;  // copy instructions per wave per block
   // One array per ring stage: distinct LDS objects let the compiler tell the
   // stages apart, so a read of one stage does not wait for the copies still
   // in flight into the others.
@@ -217,8 +164,8 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qr[kk] = ld_bf16x8(qp + 16 * kk);
   }
-  LanesX<D> tl(hf, lq);
-  const BlockLoader<D, kFwdWaves> ldr(wave, lane);
+  LanesCM<D> tl(hf, lq);
+  const BlockLoaderCM<D, kFwdWaves> ldr(wave, lane);
 
   f32x16 acc[NMT];
   float mref = -kInf;   // exp2 shift of this query (log2 units)
@@ -257,8 +204,8 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         const size_t off = LS_BLOCK_OFF(j);
-        load_block(ldr, kst[j], a.k + off, kBN);
-        load_block(ldr, vst[j], a.v + off, kBN);
+        load_block_cm<false>(ldr, kst[j], a.k + off, kBN);
+        load_block_cm<true>(ldr, vst[j], a.v + off, kBN);
       }
       float mlane = -kInf;  // running max of this lane's raw scores in the range
       // Values the loop reads that may have been reloaded from scratch: make
@@ -307,8 +254,8 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
         int nv, key0;
         const size_t off = walk.block(j, nv, key0);
         if (nv > 0) {
-          load_block(ldr, k0, a.k + off, nv);
-          load_block(ldr, v0, a.v + off, nv);
+          load_block_cm<false>(ldr, k0, a.k + off, nv);
+          load_block_cm<true>(ldr, v0, a.v + off, nv);
         }
         wait_loads_le<0>();
         __syncthreads();
