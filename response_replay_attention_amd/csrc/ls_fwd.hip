@@ -57,7 +57,7 @@ __device__ __forceinline__ void fwd_step(const LanesCM<D>& tl, const BlockLoader
                                          int hf = 0, int kmin = -0x7fffffff) {
   constexpr int NS = D / 16;   // score MFMAs per step = PV MFMAs per step
   constexpr int NMT = D / 32;  // 32-wide d tiles of O^T
-  constexpr int PF = 1;        // LDS prefetch distance, in MFMAs
+  constexpr int PF = 2;        // LDS prefetch distance, in MFMAs (3 spills in the loop)
   constexpr int NIW = BlockLoaderCM<D, kFwdWaves>::NIW;
   constexpr int CEV = NS / (2 * NIW);  // PV segments per copy instruction
   static_assert(CEV * 2 * NIW == NS, "copy instructions spread evenly over the PV MFMAs");
