@@ -130,44 +130,6 @@ struct Lanes32 {
   }
 };
 
-// The same operand addresses in two registers instead of sixteen.  In every
-// address above the lane-dependent part and the swizzled chunk field occupy
-// disjoint bits, so
-//     rb[k7]     = rbx ^ (16*k7)            rbx = lq*D | 8*(hf ^ swf(lq))
-//     tb[c][m3]  = tbx ^ (16*c + 32*m3)     tbx = (4*hf + e)*D | 4*(L & 1)
-//                                                 | 8*(b0 | 2*g1 | 4*e)
-// and each read costs one v_xor.  refresh() hides the two bases from
-// loop-invariant code motion, which would otherwise precompute all sixteen
-// addresses again.  Used where the register budget is 256 per wave.
-template <int D>
-struct LanesX {
-  int rbx, tbx;
-  __device__ __forceinline__ LanesX(int hf, int lq) {
-    rbx = (lq * D) | (8 * (hf ^ swf(lq)));
-    const int L = lq & 15, g1 = (lq >> 4) & 1, e = L >> 2;
-    const int b0 = ((L >> 1) & 1) ^ hf;
-    tbx = ((4 * hf + e) * D) | (4 * (L & 1)) | (8 * (b0 | 2 * g1 | 4 * e));
-  }
-  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(rbx), "+v"(tbx)); }
-  __device__ __forceinline__ bf16x8 row8(const uint16_t* tile, int kk) const {
-    return ld_bf16x8(tile + (rbx ^ (16 * (kk & 7))) + 128 * (kk >> 3));
-  }
-  __device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int ks, int mt) const {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const uint16_t* base = tile + 16 * ks * D + 128 * (mt >> 2);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(base + (tbx ^ (32 * (mt & 3)))));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(base + 8 * D + (tbx ^ (16 + 32 * (mt & 3)))));
-    const s16x4 v[2] = {lo, hi};
-    u16x8 r;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) r[t] = (unsigned short)v[t >> 2][t & 3];
-    return __builtin_bit_cast(bf16x8, r);
-  }
-};
-
 // Forward tiles in chunk-major layouts.  K keeps the 16-byte chunk c (elements
 // [8c, 8c+8)) of key row r in 16-byte slot c*32 + r; V keeps chunk C of row r
 // in slot C*32 + (r ^ 4*(C & 3)).  With these, every operand read is one
@@ -246,16 +208,6 @@ struct TileLoader {
     }
   }
 };
-
-// Free-function form of TileLoader::load.  Kernels call this rather than the
-// member from inside lambdas: the HIP front end (ROCm 7.2 clang) silently drops
-// the host launch stub of some kernel template instantiations when a lambda in
-// the kernel calls a member function of a captured TileLoader.
-template <int D, int NW>
-__device__ __forceinline__ void load_tile(const TileLoader<D, NW>& t, uint16_t* tile,
-                                          const uint16_t* g, int nvalid) {
-  t.load(tile, g, nvalid);
-}
 
 // One-shot form of TileLoader::load (for kernels that load few tiles).
 template <int D, int NW = 4>
