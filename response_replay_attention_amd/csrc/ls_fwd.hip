@@ -151,7 +151,15 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   const size_t row0 = (size_t)kv * GR;
   const KeyWalk<D, RESP> walk(a, kv, unit, m0, kFwdRows);
   const int nblocks = walk.nblocks;
-  const int nfull = walk.nfull;          // leading blocks that need no mask
+  // leading blocks that need no mask: the full prompt pages of the range or,
+  // in the response block of one response when the tile stays in one query
+  // head, the keys that even the tile's first row sees (these then stream
+  // through the ring like prompt blocks)
+  int nfull = walk.nfull;
+  if (RESP && !a.moffs) {
+    const int mlast = min(m0 + kFwdRows, GR) - 1;
+    if (m0 / a.R == mlast / a.R) nfull = min((a.qoff + m0 % a.R + 1) / kBN, nblocks);
+  }
   const int slot = a.slot_base + unit;
 
   // Q (B operand): column = query m, k = 16*kk + 8*hf + e.  Rows past the
@@ -196,11 +204,18 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
       // pool offsets of page pn and pn+1, and the id of page pn+2 (loaded one
       // page ahead of its use); copies address block j through page j / BPP
       int pn = 0;
-      size_t base0 = walk.page_base(walk.page_id(0));
-      size_t base1 = npg > 1 ? walk.page_base(walk.page_id(1)) : 0;
-      int id2 = npg > 2 ? walk.page_id(2) : -1;
+      size_t base0 = 0, base1 = 0;
+      int id2 = -1;
+      if (!RESP) {
+        base0 = walk.page_base(walk.page_id(0));
+        base1 = npg > 1 ? walk.page_base(walk.page_id(1)) : 0;
+        id2 = npg > 2 ? walk.page_id(2) : -1;
+      }
+      // (response keys are contiguous: block j is rows [32j, 32j+32) of this KV head)
 #define LS_BLOCK_OFF(j)                                                              \
-  ((j) < nfull ? (((j) / BPP == pn) ? base0 : base1) + ((j) % BPP) * kBlk : (size_t)0)
+  ((j) < nfull ? (RESP ? ((size_t)kv * a.kvr + (size_t)(j) * kBN) * D                 \
+                       : (((j) / BPP == pn) ? base0 : base1) + ((j) % BPP) * kBlk)      \
+               : (size_t)0)
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         const size_t off = LS_BLOCK_OFF(j);
@@ -227,7 +242,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   }
       for (int b = 0; b < nfull; b += NST) {
         // the copies of this iteration (blocks b+3 .. b+6) reach page (b+6)/BPP
-        if ((b + 6) / BPP > pn + 1 && b + 6 < nfull) {
+        if (!RESP && (b + 6) / BPP > pn + 1 && b + 6 < nfull) {
           ++pn;
           base0 = base1;
           base1 = walk.page_base(id2);
