@@ -32,18 +32,36 @@ __global__ void __launch_bounds__(256) k_merge(int nper, int64_t rows, const flo
   }
   float tot = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // parts are added in index order; four parts' loads are issued together
+  // (an empty part has l = 0 and o = 0, so it adds exactly nothing)
+  auto add = [&](const float4& o, float w) {
+    tot += w;
+    acc.x += w * o.x;
+    acc.y += w * o.y;
+    acc.z += w * o.z;
+    acc.w += w * o.w;
+  };
   if (big != -kInf) {
-    for (int c = 0; c < nper; ++c) {
+    int c = 0;
+    for (; c + 4 <= nper; c += 4) {
+      float4 o[4];
+      float w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t i = (size_t)(c0 + c + u) * rows + row;
+        o[u] = *reinterpret_cast<const float4*>(po + i * D + 4 * e4);
+        const float l = pl[i];
+        w[u] = l > 0.f ? l * expf(pm[i] - big) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (w[u] > 0.f) add(o[u], w[u]);
+    }
+    for (; c < nper; ++c) {
       const size_t i = (size_t)(c0 + c) * rows + row;
       const float l = pl[i];
       if (!(l > 0.f)) continue;
-      const float w = l * expf(pm[i] - big);
-      tot += w;
-      const float4 o = *reinterpret_cast<const float4*>(po + i * D + 4 * e4);
-      acc.x += w * o.x;
-      acc.y += w * o.y;
-      acc.z += w * o.z;
-      acc.w += w * o.w;
+      add(*reinterpret_cast<const float4*>(po + i * D + 4 * e4), l * expf(pm[i] - big));
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
