@@ -119,6 +119,32 @@ def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: s
     return t.data_ptr()
 
 
+def _expect(t, shape, name: str) -> None:
+    """The kernels trust the sizes in the shape struct: a tensor that does not
+    match them would be read or written out of bounds, so refuse it here."""
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if tuple(int(x) for x in t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _expect_at_least(t, numel: int, name: str) -> None:
+    if t is None or t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements")
+
+
+def _check_attn_tensors(shape: "AttnShape", pt: "PageTable", q, k_pool, v_pool, k_resp, v_resp,
+                        nparts: Optional[int] = None) -> None:
+    hq, hkv, d, R = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.resp_len
+    kvr = shape.kv_rows if shape.kv_rows else shape.q_offset + R
+    _expect(q, (hq, R, d), "q")
+    _expect(k_resp, (hkv, kvr, d), "k_resp")
+    _expect(v_resp, (hkv, kvr, d), "v_resp")
+    if pt.num_pages > 0:
+        _expect(k_pool, (pt.num_phys_pages, hkv, shape.page_size, d), "k_pool")
+        _expect(v_pool, (pt.num_phys_pages, hkv, shape.page_size, d), "v_pool")
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -173,6 +199,11 @@ def ls_replay_attn_bwd_workspace(shape: AttnShape, pt: PageTable) -> int:
 def ls_replay_attn_fwd(shape: AttnShape, pt: PageTable, q, k_pool, v_pool, k_resp, v_resp,
                        part_o, part_m, part_l, workspace=None, stream=None) -> None:
     bf, f32 = torch.bfloat16, torch.float32
+    _check_attn_tensors(shape, pt, q, k_pool, v_pool, k_resp, v_resp)
+    rows = (pt.num_splits + 1) * shape.num_q_heads * shape.resp_len
+    _expect_at_least(part_o, rows * shape.head_dim, "part_o")
+    _expect_at_least(part_m, rows, "part_m")
+    _expect_at_least(part_l, rows, "part_l")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ls_replay_attn_fwd(
         ctypes.byref(shape), ctypes.byref(pt), _ptr(q, bf, "q"), _ptr(k_pool, bf, "k_pool"),
@@ -188,7 +219,14 @@ def ls_replay_attn_fwd_members(shape: AttnShape, pt: PageTable, member_offsets, 
     """``member_offsets``: host int32 numpy array [G+1]; ``member_offsets_dev``: its device copy
     (an int32 tensor), or None for one member."""
     bf, f32 = torch.bfloat16, torch.float32
+    _check_attn_tensors(shape, pt, q, k_pool, v_pool, k_resp, v_resp)
+    rows = (pt.num_splits + 1) * shape.num_q_heads * shape.resp_len
+    _expect_at_least(part_o, rows * shape.head_dim, "part_o")
+    _expect_at_least(part_m, rows, "part_m")
+    _expect_at_least(part_l, rows, "part_l")
     offs = np.ascontiguousarray(member_offsets, dtype=np.int32)
+    if member_offsets_dev is not None:
+        _expect(member_offsets_dev, (offs.size,), "member_offsets_dev")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dev_ptr = 0 if member_offsets_dev is None else _ptr(member_offsets_dev, torch.int32, "member_offsets_dev")
     st = lib().ls_replay_attn_fwd_members(
@@ -208,6 +246,10 @@ def ls_kv_page_append(k_chunk, v_chunk, slots, slots_dev, k_pool, v_pool, stream
     sl = np.ascontiguousarray(slots, dtype=np.int32)
     if sl.size != (tokens + PAGE_SIZE - 1) // PAGE_SIZE:
         raise ValueError(f"slots: expected {(tokens + PAGE_SIZE - 1) // PAGE_SIZE} entries, got {sl.size}")
+    _expect(v_chunk, (hkv, tokens, d), "v_chunk")
+    _expect(slots_dev, (sl.size,), "slots_dev")
+    _expect(k_pool, (int(k_pool.shape[0]), hkv, PAGE_SIZE, d), "k_pool")
+    _expect(v_pool, tuple(k_pool.shape), "v_pool")
     st = lib().ls_kv_page_append(
         hkv, d, tokens, _ptr(k_chunk, bf, "k_chunk"), _ptr(v_chunk, bf, "v_chunk"),
         sl.ctypes.data, _ptr(slots_dev, torch.int32, "slots_dev"), _ptr(k_pool, bf, "k_pool"),
@@ -218,6 +260,11 @@ def ls_kv_page_append(k_chunk, v_chunk, slots, slots_dev, k_pool, v_pool, stream
 def ls_lse_merge(num_parts: int, rows: int, head_dim: int, part_o, part_m, part_l, o_bf16, lse,
                  stream=None) -> None:
     f32 = torch.float32
+    _expect_at_least(part_o, num_parts * rows * head_dim, "part_o")
+    _expect_at_least(part_m, num_parts * rows, "part_m")
+    _expect_at_least(part_l, num_parts * rows, "part_l")
+    _expect_at_least(o_bf16, rows * head_dim, "o")
+    _expect_at_least(lse, rows, "lse")
     st = lib().ls_lse_merge(num_parts, rows, head_dim, _ptr(part_o, f32, "part_o"),
                             _ptr(part_m, f32, "part_m"), _ptr(part_l, f32, "part_l"),
                             _ptr(o_bf16, torch.bfloat16, "o"), _ptr(lse, f32, "lse"),
@@ -228,6 +275,14 @@ def ls_lse_merge(num_parts: int, rows: int, head_dim: int, part_o, part_m, part_
 def ls_replay_attn_bwd(shape: AttnShape, pt: PageTable, q, k_pool, v_pool, k_resp, v_resp, o, lse,
                        d_o, dq, dk_resp, dv_resp, workspace, stream=None) -> None:
     bf, f32 = torch.bfloat16, torch.float32
+    _check_attn_tensors(shape, pt, q, k_pool, v_pool, k_resp, v_resp)
+    hq, hkv, d, R = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.resp_len
+    kvr = shape.kv_rows if shape.kv_rows else shape.q_offset + R
+    for t, name in ((o, "o"), (d_o, "d_o"), (dq, "dq")):
+        _expect(t, (hq, R, d), name)
+    _expect_at_least(lse, hq * R, "lse")
+    _expect(dk_resp, (hkv, kvr, d), "dk_resp")
+    _expect(dv_resp, (hkv, kvr, d), "dv_resp")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ls_replay_attn_bwd(
         ctypes.byref(shape), ctypes.byref(pt), _ptr(q, bf, "q"), _ptr(k_pool, bf, "k_pool"),

@@ -342,3 +342,37 @@ def test_token_block_shape_accepted_and_sized():
 
 def test_members_reject_q_offset():
     assert _fwd_members(_shape(q_offset=32), _table(), [0, 32, 64]) == INVALID
+
+
+# ------------------------------------------------------ binding size checks
+
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(*shape, dtype=dtype)
+
+
+def test_binding_refuses_tensors_that_do_not_match_the_shape():
+    """The kernels trust the shape struct; the binding refuses tensors whose
+    sizes disagree with it before any library call."""
+    sh = B.make_shape(6, 2, 128, 0, 40, 0.1, q_offset=24)
+    pt = B.PageTable(0, 0, 0, 0, 0, 1, 0)
+    q, kr = _t(6, 40, 128), _t(2, 64, 128)
+    po, pm = _t(2, 6, 40, 128, dtype=torch.float32), _t(2, 6, 40, dtype=torch.float32)
+    with pytest.raises(ValueError, match="k_resp"):      # needs q_offset + R = 64 rows
+        B.ls_replay_attn_fwd(sh, pt, q, None, None, _t(2, 63, 128), kr, po, pm, pm)
+    with pytest.raises(ValueError, match="q"):
+        B.ls_replay_attn_fwd(sh, pt, _t(6, 41, 128), None, None, kr, kr, po, pm, pm)
+    with pytest.raises(ValueError, match="part_o"):
+        B.ls_replay_attn_fwd(sh, pt, q, None, None, kr, kr, po[:1], pm, pm)
+    f32 = torch.float32
+    with pytest.raises(ValueError, match="dk_resp"):
+        B.ls_replay_attn_bwd(sh, pt, q, None, None, kr, kr, q, _t(6, 40, dtype=f32), q,
+                             _t(6, 40, 128, dtype=f32), _t(2, 40, 128, dtype=f32),
+                             _t(2, 64, 128, dtype=f32), None)
+    with pytest.raises(ValueError, match="part_o"):
+        B.ls_lse_merge(3, 6 * 40, 128, po, pm, pm, q, _t(6, 40, dtype=f32))
+    k = _t(2, 300, 128)
+    pool = _t(4, 2, 256, 128)
+    with pytest.raises(ValueError, match="v_chunk"):
+        B.ls_kv_page_append(k, _t(2, 299, 128), [0, 1], torch.zeros(2, dtype=torch.int32), pool, pool)
+    with pytest.raises(ValueError, match="k_pool"):
+        B.ls_kv_page_append(k, k, [0, 1], torch.zeros(2, dtype=torch.int32), _t(4, 2, 256, 64), pool)
