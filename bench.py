@@ -60,12 +60,21 @@ def flops(shape) -> dict:
 
 
 def source_digest() -> str:
+    """Hash of the kernel sources with comments and blank space taken out, so
+    that a counter summary stays attached to the code it measured across
+    edits that change no code."""
+    import re
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "response_replay_attention_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp", ".cpp", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name)) as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            text = " ".join(text.split())
+            h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

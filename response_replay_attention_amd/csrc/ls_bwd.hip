@@ -7,8 +7,9 @@
 //     the saved LSE -- one partial per split, later summed in split order (the
 //     one-GPU stand-in for the pages' dQ all-reduce across CP ranks);
 //   * dQ over the causal response block (one more partial);
-//   * dK, dV of the response keys (KV-stationary, summed over the query heads
-//     of each KV group inside one workgroup, so no atomics are needed).
+//   * dK, dV of the response keys (key-stationary, one partial per query head,
+//     summed over the heads of each KV group in head order by k_kv_reduce, so
+//     no atomics are needed).
 //
 // dQ kernel mapping (4 waves x 32 query rows): per key block
 //   S^T  = K Q^T      (A = K rows from LDS, B = Q in registers)
