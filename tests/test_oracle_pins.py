@@ -219,6 +219,32 @@ def test_subset_rows_give_exact_tail_key_gradients():
     np.testing.assert_allclose(dvr2[:, 15:], dvr[:, 15:], atol=1e-13, rtol=0)
 
 
+def test_row_block_contributions_match_masked_autograd():
+    """A token block's rows alone (the oracle's rows= subset, as the token-block
+    replay uses it) give what autograd gives for <dO, O> with dO zero outside
+    the block: rows with dO = 0 have dP = 0 and D = 0, so they add nothing.
+    The blocks' contributions then sum to the whole response's gradient."""
+    q, kp, vp, kr, vr, do = _problem(6, 2, 16, 37, 23, seed=29)
+    s = 0.25
+    _, dkr_all, dvr_all, _, _ = oracle.replay_backward(q, kp, vp, kr, vr, do, s)
+    dk_sum, dv_sum = np.zeros_like(dkr_all), np.zeros_like(dvr_all)
+    for b0, b1 in ((0, 6), (6, 13), (13, 23)):
+        rows = np.tile(np.arange(b0, b1), (6, 1))
+        dq_b, dk_b, dv_b, _, _ = oracle.replay_backward(q, kp, vp, kr, vr, do, s, rows=rows)
+        out, (tq, _, _, tkr, tvr) = _full_sequence_sdpa(q, kp, vp, kr, vr, s, grad=True)
+        mask = np.zeros_like(do)
+        mask[:, b0:b1] = 1.0
+        (out * torch.tensor(do * mask)).sum().backward()
+        np.testing.assert_allclose(dk_b, tkr.grad.numpy(), atol=1e-11, rtol=0)
+        np.testing.assert_allclose(dv_b, tvr.grad.numpy(), atol=1e-11, rtol=0)
+        np.testing.assert_allclose(dq_b, tq.grad.numpy()[:, b0:b1], atol=1e-11, rtol=0)
+        assert not dk_b[:, b1:].any() and not dv_b[:, b1:].any()   # keys after the block
+        dk_sum += dk_b
+        dv_sum += dv_b
+    np.testing.assert_allclose(dk_sum, dkr_all, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv_sum, dvr_all, atol=1e-12, rtol=0)
+
+
 def _split_parts(q, kp, vp, kr, vr, s, order, offsets):
     """Per-split statistics for every (head,row), the response block last."""
     hq, r, d = q.shape
