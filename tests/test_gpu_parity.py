@@ -239,3 +239,44 @@ def test_side_stream_gives_the_same_bits():
         assert torch.equal(fwd.o, ref.o) and torch.equal(fwd.lse, ref.lse)
         for a, b in zip(g, ref_g):
             assert torch.equal(a, b)
+
+
+def test_hand_worked_example():
+    """The replay worked by hand in tests/golden, zero-padded to d = 128, through
+    the C ABI: the prompt's two keys sit in a partial page in pool slot 1."""
+    import json
+    import os
+    print("case hand worked example", flush=True)
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked_example.json")))
+    env = {"ln": math.log}
+    val = lambda x: float(eval(x, {"__builtins__": {}}, env)) if isinstance(x, str) else float(x)  # noqa: E731
+    scale = val(g["scale"])
+    D = 128
+
+    def pad(rows):
+        t = torch.zeros(len(rows), D, dtype=torch.float32)
+        t[:, :2] = torch.tensor(rows, dtype=torch.float32)
+        return t
+
+    inp = g["inputs"]
+    q = pad(inp["q"])[None].to("cuda", torch.bfloat16)
+    d_o = pad(inp["d_o"])[None].to("cuda", torch.bfloat16)
+    k_resp = pad(inp["k_resp"])[None].to("cuda", torch.bfloat16)
+    v_resp = pad(inp["v_resp"])[None].to("cuda", torch.bfloat16)
+    k_pool = torch.randn(2, 1, 256, D).to("cuda", torch.bfloat16)   # junk everywhere else
+    v_pool = torch.randn(2, 1, 256, D).to("cuda", torch.bfloat16)
+    k_pool[1, 0, :2] = pad(inp["k_prompt"]).to("cuda", torch.bfloat16)
+    v_pool[1, 0, :2] = pad(inp["v_prompt"]).to("cuda", torch.bfloat16)
+    cache = PromptCache(k_pool, v_pool, 2, [1], 1)
+    fwd = replay_forward(cache, q, k_resp, v_resp, scale)
+    dq, dk, dv = replay_backward(cache, q, k_resp, v_resp, fwd.o, fwd.lse, d_o, scale)
+    torch.cuda.synchronize()
+    exp = g["expected"]
+    grid = lambda x: np.array([[val(e) for e in row] for row in x])  # noqa: E731
+    np.testing.assert_allclose(to_np(fwd.o[0, :, :2]), grid(exp["o"]), atol=3e-3, rtol=0)
+    np.testing.assert_allclose(to_np(fwd.lse[0]), [val(e) for e in exp["lse"]], atol=2e-4, rtol=0)
+    np.testing.assert_allclose(to_np(dq[0, :, :2]), grid(exp["dq"]), atol=2e-3, rtol=0)
+    np.testing.assert_allclose(to_np(dk[0, :, :2]), grid(exp["dk_resp"]), atol=1e-3, rtol=0)
+    np.testing.assert_allclose(to_np(dv[0, :, :2]), grid(exp["dv_resp"]), atol=2e-3, rtol=0)
+    for t in (fwd.o, dq, dk, dv):   # the padding carries nothing
+        assert not bool(t[..., 2:].float().abs().max() > 0)

@@ -347,3 +347,34 @@ def test_planted_mistakes_are_caught(monkeypatch):
         assert not _sdpa_pin_holds(), bad.__name__
     monkeypatch.setattr(oatt, "_score_rows", good)
     assert _sdpa_pin_holds()
+
+
+def _golden_hand_example():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_example.json")
+    g = json.load(open(path))
+    env = {"ln": math.log}
+
+    def val(x):
+        return float(eval(x, {"__builtins__": {}}, env)) if isinstance(x, str) else float(x)
+
+    def arr(x):
+        return np.array([[val(e) for e in row] for row in x]) if isinstance(x[0], list) else np.array([val(e) for e in x])
+    inp = {k: np.array(v, dtype=np.float64) for k, v in g["inputs"].items()}
+    exp = {k: arr(v) for k, v in g["expected"].items()}
+    return inp, val(g["scale"]), exp
+
+
+def test_hand_worked_example():
+    """The oracle against a replay worked by hand (tests/golden)."""
+    inp, s, exp = _golden_hand_example()
+    q, do = inp["q"][None], inp["d_o"][None]
+    kp, vp = inp["k_prompt"][None], inp["v_prompt"][None]
+    kr, vr = inp["k_resp"][None], inp["v_resp"][None]
+    dq, dkr, dvr, o, lse = oracle.replay_backward(q, kp, vp, kr, vr, do, s)
+    np.testing.assert_allclose(o[0], exp["o"], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse[0], exp["lse"], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(dq[0], exp["dq"], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(dkr[0], exp["dk_resp"], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(dvr[0], exp["dv_resp"], atol=1e-14, rtol=0)
