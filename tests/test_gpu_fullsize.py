@@ -5,11 +5,20 @@
 * the G = 8 group replayed serially over that prefix (R = 512 ... 4096);
 * the 4,456,448-position stress prefix over 16 splits.
 
+With LS_ORACLE_FULL=1 the 262,144-position shard and the 2,097,152-position
+prefix are also checked on every row of every head, and on every key of dK_r
+and dV_r (minutes of host time: the float64 oracle runs on one thread per KV
+group).
+
 The float64 oracle computes sampled rows of every query head it checks (row 0,
 row R-1 and seeded others) plus the last TAIL rows of every head of the
 checked KV groups, which makes dK_r and dV_r exact for the last TAIL keys.  The
 Q = 0 closed form checks every row at full size at no oracle cost.
 """
+import os
+import time
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -170,3 +179,73 @@ def test_group_peak_memory_follows_longest_member():
     assert torch.cuda.memory_allocated() == base
     print(f"peak longest {peak_longest / 2**20:.1f} MiB, group {peak_group / 2**20:.1f} MiB", flush=True)
     assert peak_group <= peak_longest + (1 << 20)
+
+
+@pytest.mark.skipif(os.environ.get("LS_ORACLE_FULL") != "1",
+                    reason="every row at full size takes minutes of host time; set LS_ORACLE_FULL=1")
+@pytest.mark.timeout(3000)
+@pytest.mark.parametrize("shape", [SHARD_256K, FULL_2M], ids=["shard_262k", "prefix_2m_s8"])
+def test_full_size_every_row(shape):
+    """The whole output against the whole oracle: O, LSE and dQ of every row of
+    every query head, dK_r and dV_r of every response key of every KV head.
+
+    The oracle runs as one task per (query head, block of rows) on host
+    threads (numpy releases the GIL in its array loops and BLAS calls); each
+    task returns its rows' dQ, O, LSE and its rows' contribution to dK_r and
+    dV_r, and a KV head's dK_r / dV_r is the sum of those contributions over
+    the heads of its group and all their rows."""
+    print(f"case {shape.name} every row", flush=True)
+    inp = make_inputs(shape, seed=20260001, device="cuda")
+    _, fwd, dq, dk, dv = run(shape, inp)
+    g, P, R = shape.hq // shape.hkv, shape.prompt_len, shape.resp_len
+    got = {k: t.cpu() for k, t in (("o", fwd.o), ("lse", fwd.lse), ("dq", dq), ("dk", dk), ("dv", dv))}
+    prompts = [(oracle.as_f64(logical_prompt(inp["k_pool"], inp["l2p"], P, kv_heads=[kv])),
+                oracle.as_f64(logical_prompt(inp["v_pool"], inp["l2p"], P, kv_heads=[kv])))
+               for kv in range(shape.hkv)]
+    resp = {k: oracle.as_f64(inp[k]) for k in ("q", "d_o", "k_resp", "v_resp")}
+    del inp, fwd, dq, dk, dv
+    torch.cuda.empty_cache()
+    rows_per_task = 256   # each task copies its KV head's prompt once: keep the tasks few
+    tasks = [(h, r0) for h in range(shape.hq) for r0 in range(0, R, rows_per_task)]
+    t_start = time.time()
+
+    def task(t):
+        h, r0 = t
+        kv = h // g
+        rows = np.arange(r0, min(R, r0 + rows_per_task), dtype=np.int64)[None]
+        out = oracle.replay_backward(resp["q"][h:h + 1], prompts[kv][0], prompts[kv][1],
+                                     resp["k_resp"][kv:kv + 1], resp["v_resp"][kv:kv + 1],
+                                     resp["d_o"][h:h + 1], shape.scale, rows=rows)
+        print(f"  oracle head {h} rows [{r0}, {r0 + rows.shape[1]}): {time.time() - t_start:.0f} s",
+              flush=True)
+        return out
+
+    # one BLAS thread per task (several BLAS pools spinning at once stall each
+    # other), and no more tasks at once than ~150 GB of host memory holds: each
+    # concatenates its KV head's prompt and response keys and values, and
+    # holds a few [64, P + R] float64 temporaries
+    per_task = 2 * (P + R) * shape.head_dim * 8 + 6 * 64 * (P + R) * 8
+    workers = int(os.environ.get("LS_ORACLE_THREADS", "0")) or max(
+        1, min(len(os.sched_getaffinity(0)), 16, (150 << 30) // per_task))
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=workers) as ex:
+        results = list(ex.map(task, tasks))
+    print(f"  oracle host time {time.time() - t_start:.0f} s on {workers} threads", flush=True)
+    o_r = np.zeros((shape.hq, R, shape.head_dim))
+    dq_r = np.zeros_like(o_r)
+    lse_r = np.zeros((shape.hq, R))
+    dk_r = np.zeros((shape.hkv, R, shape.head_dim))
+    dv_r = np.zeros_like(dk_r)
+    for (h, r0), (dq_t, dk_t, dv_t, o_t, lse_t) in zip(tasks, results):
+        n = o_t.shape[1]
+        o_r[h, r0:r0 + n], dq_r[h, r0:r0 + n], lse_r[h, r0:r0 + n] = o_t[0], dq_t[0], lse_t[0]
+        dk_r[h // g] += dk_t[0]
+        dv_r[h // g] += dv_t[0]
+    m = {"O": assert_close("O", got["o"], o_r),
+         "dQ": assert_close("dQ", got["dq"], dq_r),
+         "dK_r": assert_close("dK_r", got["dk"], dk_r),
+         "dV_r": assert_close("dV_r", got["dv"], dv_r)}
+    lse_rel = assert_lse_close("LSE", got["lse"], lse_r)
+    print(f"  LSE rel {lse_rel:.2e}; "
+          + "; ".join(f"{k} max_abs {v['max_abs']:.2e} rel_l2 {v['rel_l2']:.2e}" for k, v in m.items()),
+          flush=True)
