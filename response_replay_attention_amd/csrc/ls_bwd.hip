@@ -11,11 +11,12 @@
 //     summed over the heads of each KV group in head order by k_kv_reduce, so
 //     no atomics are needed).
 //
-// dQ kernel mapping (4 waves x 32 query rows): per key block
-//   S^T  = K Q^T      (A = K rows from LDS, B = Q in registers)
-//   dP^T = V dO^T     (A = V rows from LDS, B = dO in registers)
+// dQ kernel mapping (32 query rows per score wave and per dQ wave): per key block
+//   S^T  = K Q^T      (A = K rows from LDS, B = Q in the score wave's registers)
+//   dP^T = V dO^T     (A = V rows from LDS, B = dO in the score wave's registers)
 //   dS^T = P^T (dP^T - D)                    with P^T = exp2(S^T*s*log2e - LSE*log2e)
-//   dQ^T += K^T dS^T  (A = K^T gathered from the same K tile, B = dS^T in registers)
+//   dQ^T += K^T dS^T  (A = K^T gathered from the same K tile, B = dS^T that the
+//                      score wave stored to LDS, in the dQ wave)
 // so dQ^T keeps one query per lane, like O^T in the forward.
 #include "ls_device.hpp"
 
@@ -60,108 +61,99 @@ __device__ __forceinline__ void block_dq(f32x16 (&acc)[D / 32], const Lanes32<D>
   }
 }
 
-// One pipelined step of the prompt dQ loop: S(b+1) = K(b+1) Q^T and
-// dP(b+1) = V(b+1) dO^T, dS(b) on the VALU, then dQ^T += K(b)^T dS(b)^T, and
-// the copies of K(b+3) and V(b+4).  As in the forward, the step is a fixed
-// sequence of sched_barrier-fenced micro-segments that keeps the wave's LDS
-// read stream continuous: one MFMA each, the operand read PF MFMAs ahead, one
-// dS element every second score segment, one copy every second dQ segment.
+// One block of a score wave: S^T = K Q^T and dP^T = V dO^T (the two products
+// interleaved, each operand read PF MFMAs ahead), then dS^T = P^T (dP^T - D),
+// stored to dsw as the two bf16 B operands of the dQ product, in this lane's
+// register order ([ks][lane][8] elements), for the dQ wave of the same rows.
 template <int D>
-__device__ __forceinline__ void bwd_step(const Lanes32<D>& tl, const BlockLoader<D>& ldr,
-                                         const uint16_t* kn, const uint16_t* vn,
-                                         const uint16_t* kc, const bf16x8 (&qr)[D / 16],
-                                         const bf16x8 (&dor)[D / 16], f32x16& s_cur,
-                                         f32x16& dp_cur, f32x16 (&acc)[D / 32], float s2,
-                                         float lse2, float dval, uint32_t kdst, i32x4 kdesc,
-                                         uint32_t vdst, i32x4 vdesc) {
-  constexpr int NS = D / 16;   // k-steps of the score products = dQ MFMAs per step
-  constexpr int NA = 2 * NS;   // score + dP MFMAs per step
-  constexpr int NMT = D / 32;
-  constexpr int PF = 4;        // LDS prefetch distance, in MFMAs
-  constexpr int NIW = BlockLoader<D>::NIW;
-  static_assert(2 * NIW * 2 == NS, "one copy instruction every second dQ MFMA");
-  bf16x8 rf[NA], cf[NS];
+__device__ __forceinline__ void score_block(const Lanes32<D>& tl, const uint16_t* kt,
+                                            const uint16_t* vt, const bf16x8 (&qr)[D / 16],
+                                            const bf16x8 (&dor)[D / 16], float s2, float lse2,
+                                            float dval, uint16_t* dsw) {
+  constexpr int NS = D / 16;
+  constexpr int NA = 2 * NS;  // score + dP MFMAs per block
+  constexpr int PF = 4;       // LDS prefetch distance, in MFMAs
+  bf16x8 rf[NA];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) rf[i] = (i & 1) ? tl.row8(vn, i >> 1) : tl.row8(kn, i >> 1);
-  f32x16 s_next, dp_next;
+  for (int i = 0; i < PF; ++i) rf[i] = (i & 1) ? tl.row8(vt, i >> 1) : tl.row8(kt, i >> 1);
+  f32x16 s, dp;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s_next[r] = 0.f;
-    dp_next[r] = 0.f;
+    s[r] = 0.f;
+    dp[r] = 0.f;
   }
-  bf16x8 dsb[2];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    if (i & 1) dp_next = mfma32(rf[i], dor[i >> 1], dp_next);
-    else s_next = mfma32(rf[i], qr[i >> 1], s_next);
+    if (i & 1) dp = mfma32(rf[i], dor[i >> 1], dp);
+    else s = mfma32(rf[i], qr[i >> 1], s);
     if (i + PF < NA) {
       const int n = i + PF;
-      rf[n] = (n & 1) ? tl.row8(vn, n >> 1) : tl.row8(kn, n >> 1);
-    } else {
-      const int j = i + PF - NA;
-      cf[j] = tl.col8(kc, j / NMT, j % NMT);
-    }
-    if (i & 1) {
-#pragma unroll
-      for (int r = (i >> 1) * 16 / NS; r < ((i >> 1) + 1) * 16 / NS; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], s2, -lse2));
-        dsb[r >> 3][r & 7] = to_bf16(p * (dp_cur[r] - dval));
-      }
+      rf[n] = (n & 1) ? tl.row8(vt, n >> 1) : tl.row8(kt, n >> 1);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  bf16x8 dsb[2];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    acc[j % NMT] = mfma32(cf[j], dsb[j / NMT], acc[j % NMT]);
-    if (j + PF < NS) cf[j + PF] = tl.col8(kc, (j + PF) / NMT, (j + PF) % NMT);
-    if ((j & 1) == 0) {
-      const int c = j >> 1;
+  for (int r = 0; r < 16; ++r) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], s2, -lse2));
+    dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - dval));
+  }
+  *reinterpret_cast<bf16x8*>(dsw) = dsb[0];
+  *reinterpret_cast<bf16x8*>(dsw + 64 * 8) = dsb[1];
+}
+
+// One step of a dQ wave: dQ^T += K^T dS^T for the block whose K tile is kc and
+// whose dS^T the score wave stored at dsr (when mma), and this wave's share of
+// the copies of two ring blocks (K into kdst, V into vdst), one copy
+// instruction every second MFMA.
+template <int D>
+__device__ __forceinline__ void dq_block(const Lanes32<D>& tl, const BlockLoader<D>& ldr,
+                                         const uint16_t* kc, const uint16_t* dsr,
+                                         f32x16 (&acc)[D / 32], bool mma, uint32_t kdst,
+                                         i32x4 kdesc, uint32_t vdst, i32x4 vdesc) {
+  constexpr int NS = D / 16;  // dQ MFMAs per block
+  constexpr int NMT = D / 32;
+  constexpr int PF = 4;
+  constexpr int NIW = BlockLoader<D>::NIW;
+  static_assert(2 * NIW * 2 == NS, "one copy instruction every second dQ MFMA");
+  if (mma) {
+    bf16x8 dsb[2], cf[NS];
+    dsb[0] = *reinterpret_cast<const bf16x8*>(dsr);
+    dsb[1] = *reinterpret_cast<const bf16x8*>(dsr + 64 * 8);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) cf[j] = tl.col8(kc, j / NMT, j % NMT);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      acc[j % NMT] = mfma32(cf[j], dsb[j / NMT], acc[j % NMT]);
+      if (j + PF < NS) cf[j + PF] = tl.col8(kc, (j + PF) / NMT, (j + PF) % NMT);
+      if ((j & 1) == 0) {
+        const int c = j >> 1;
+        if (c < NIW) copy16_to_lds(kdst + ldr.lds0 + c * 1024, ldr.voff[c], kdesc);
+        else copy16_to_lds(vdst + ldr.lds0 + (c - NIW) * 1024, ldr.voff[c - NIW], vdesc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 2 * NIW; ++c) {
       if (c < NIW) copy16_to_lds(kdst + ldr.lds0 + c * 1024, ldr.voff[c], kdesc);
       else copy16_to_lds(vdst + ldr.lds0 + (c - NIW) * 1024, ldr.voff[c - NIW], vdesc);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
-  s_cur = s_next;
-  dp_cur = dp_next;
 }
 
+// The score waves' side of k_bwd_dq (the barrier sequence matches dq_role's).
 template <int D, bool RESP>
-__global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
+__device__ __forceinline__ void score_role(const AttnArgs& a, const KeyWalk<D, RESP>& walk,
+                                           const Lanes32<D>& tl, uint16_t* const (&kst)[kStages],
+                                           uint16_t* const (&vst)[kStages], uint16_t* dsw,
+                                           size_t row, bool rvalid, int qi, int hf) {
   constexpr int NKK = D / 16;
-  constexpr int NMT = D / 32;
-  constexpr int TILE = kBN * D;
-  constexpr int NST = kStages;
-  constexpr int NIW = BlockLoader<D>::NIW;  // copy instructions per wave per tile
-  static_assert(NST == 4, "the ring has four stages");
-  // one array per ring stage (distinct LDS objects; see the forward kernel)
-  __shared__ __attribute__((aligned(1024))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
-  uint16_t* const kst[NST] = {k0, k1, k2, k3};
-  uint16_t* const vst[NST] = {v0, v1, v2, v3};
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hf = lane >> 5, lq = lane & 31;
-
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_unit = a.mtiles * a.hkv;
-  const int unit = w / per_unit;
-  const int rem = w - unit * per_unit;
-  const int kv = rem / a.mtiles;
-  const int mtile = rem - kv * a.mtiles;
-  const int GR = (a.hq / a.hkv) * a.R;
-  const int m0 = mtile * kBwdRows;
-  const int m = m0 + 32 * wave + lq;
-  const bool rvalid = m < GR;
-  const size_t row0 = (size_t)kv * GR;
-  const size_t row = row0 + min(m, GR - 1);
-  const int qi = m % a.R;
-
-  const KeyWalk<D, RESP> walk(a, kv, unit, m0, kBwdRows);
-  const int nblocks = walk.nblocks;
-  const int nfull = walk.nfull;
-  const int slot = a.slot_base + unit;
-
+  constexpr int NIW = BlockLoader<D>::NIW;
+  constexpr int DSX = 2 * 64 * 8;
+  const int nblocks = walk.nblocks, nfull = walk.nfull;
   // Q and dO as B operands (column = query m, k = 16*kk + 8*hf + e)
   bf16x8 qr[NKK], dor[NKK];
   {
@@ -177,86 +169,35 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
   const float lse2 = rvalid ? a.lse[row] * kLog2e : kInf;
   const float dval = rvalid ? a.dvals[row] : 0.f;
 
-  f32x16 acc[NMT];
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
-
-  const Lanes32<D> tl(hf, lq);
-  const BlockLoader<D> ldr(wave, lane);
-
-  // ---- pipelined loop over the full (unmasked) blocks.  Step b waits for
-  // K(b+1) and V(b+1), starts K(b+3) and V(b+4), computes S(b+1) and dP(b+1)
-  // while turning S(b), dP(b) into dS(b), then accumulates K(b)^T dS(b).  K(b)
-  // stays resident for two steps (scores, then dQ), so K runs three blocks
-  // ahead and V four.  Every step issues the same number of copies (blocks
-  // past the range re-read block 0), so each wait is a fixed vmcnt.
   if (nfull > 0) {
-    wait_loads_le<0>();  // Q, dO, LSE, D have landed (the copies are invisible to the compiler)
-    // All V copies of one loop iteration (blocks b+4 .. b+7) fall in one page,
-    // whose pool offset is looked up one iteration ahead.
-    constexpr size_t kBlk = (size_t)kBN * D;
-    constexpr unsigned kBlkBytes = kBN * D * 2;
-    int ph_next = walk.page_id(0);          // page of the blocks the next iteration copies
-    size_t pcur = walk.page_base(ph_next);  // offset of the page this iteration copies from
-    size_t koff[NST];      // source offset of block j, kept from V(j)'s copy to K(j)'s
-#define LS_ISSUE_V(j, st)                                    \
-  do {                                                       \
-    koff[st] = (j) < nfull ? pcur + ((j) & 7) * kBlk : 0;    \
-    load_block(ldr, vst[st], a.v + koff[st], kBN);           \
-  } while (0)
-#define LS_ISSUE_K(st) load_block(ldr, kst[st], a.k + koff[st], kBN)
-    LS_ISSUE_V(0, 0);
-    LS_ISSUE_K(0);
-    LS_ISSUE_V(1, 1);
-    LS_ISSUE_K(1);
-    LS_ISSUE_V(2, 2);
-    LS_ISSUE_K(2);
-    LS_ISSUE_V(3, 3);
-    ring_barrier<5 * NIW>();  // V(0), K(0) landed
-    f32x16 s_cur, dp_cur;
-    block_sdp<D>(tl, kst[0], vst[0], qr, dor, s_cur, dp_cur);
-#define LS_BWD_STEP(ST)                                                                  \
-  if (b + (ST) < nfull) {                                                                \
-    /* K(b+1), V(b+1) landed; K stage ST-1 and V stage ST are free */                   \
-    ring_barrier<3 * NIW>();                                                             \
-    constexpr int SK = ((ST) + 3) % NST; /* K(b+3) goes where K(b-1) was */              \
-    const int jv = b + (ST) + 4;         /* V(b+4) goes where V(b) was */                \
-    koff[ST] = jv < nfull ? pcur + (jv & 7) * kBlk : 0;                                  \
-    bwd_step<D>(tl, ldr, kst[((ST) + 1) % NST], vst[((ST) + 1) % NST], kst[ST], qr, dor,  \
-                s_cur, dp_cur, acc, a.s2, lse2, dval, lds_addr(kst[SK]),                 \
-                block_desc(a.k + koff[SK], kBlkBytes), lds_addr(vst[ST]),                \
-                block_desc(a.v + koff[ST], kBlkBytes));                                  \
+    wait_loads_le<0>();
+#define LS_SCORE_STEP(ST)                                                                   \
+  if (b + (ST) <= nfull) {                                                                  \
+    ring_barrier<3 * NIW>();                                                                \
+    if (b + (ST) < nfull)                                                                   \
+      score_block<D>(tl, kst[ST], vst[ST], qr, dor, a.s2, lse2, dval,                       \
+                     dsw + ((ST) & 1) * 4 * DSX);                                           \
   }
-    for (int b = 0; b < nfull; b += NST) {
-      pcur = walk.page_base(ph_next);
-      ph_next = b + 8 < nfull ? walk.page_id((b + 8) >> 3) : -1;
-      LS_BWD_STEP(0)
-      LS_BWD_STEP(1)
-      LS_BWD_STEP(2)
-      LS_BWD_STEP(3)
+    for (int b = 0; b <= nfull; b += kStages) {
+      LS_SCORE_STEP(0)
+      LS_SCORE_STEP(1)
+      LS_SCORE_STEP(2)
+      LS_SCORE_STEP(3)
     }
-#undef LS_BWD_STEP
-#undef LS_ISSUE_K
-#undef LS_ISSUE_V
-    wait_loads_le<0>();  // drain the look-ahead copies before LDS is reused
-    __syncthreads();
-  }
-
-  // ---- masked blocks (partial last prompt page; the causal response block)
-  for (int j = nfull; j < nblocks; ++j) {
-    int nv, key0;
-    const size_t off = walk.block(j, nv, key0);
-    if (nv > 0) {
-      load_block(ldr, k0, a.k + off, nv);
-      load_block(ldr, v0, a.v + off, nv);
-    }
+#undef LS_SCORE_STEP
     wait_loads_le<0>();
     __syncthreads();
+  }
+
+  // masked blocks (partial last prompt page; the causal response block)
+  for (int j = nfull; j < nblocks; ++j) {
+    int nv, key0;
+    walk.block(j, nv, key0);
+    wait_loads_le<0>();
+    __syncthreads();  // the dQ waves' copies of block j have landed
     if (nv > 0) {
       f32x16 s, dp;
-      block_sdp<D>(tl, k0, v0, qr, dor, s, dp);
+      block_sdp<D>(tl, kst[0], vst[0], qr, dor, s, dp);
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -267,14 +208,104 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
       }
       bf16x8 dsb[2];
       block_ds(x, dp, a.s2, lse2, dval, dsb);
-      block_dq<D>(acc, tl, k0, dsb);
+      *reinterpret_cast<bf16x8*>(dsw) = dsb[0];
+      *reinterpret_cast<bf16x8*>(dsw + 64 * 8) = dsb[1];
     }
-    __syncthreads();  // tiles are rewritten by the next block
+    __syncthreads();  // dS of block j is stored
+    __syncthreads();  // the dQ waves have read it and the tiles
+  }
+}
+
+// The dQ waves' side of k_bwd_dq: the copies, dQ^T += K^T dS^T one block
+// behind the score waves, and the dQ partial of the 32 rows.
+template <int D, bool RESP>
+__device__ __forceinline__ void dq_role(const AttnArgs& a, const KeyWalk<D, RESP>& walk,
+                                        const Lanes32<D>& tl, uint16_t* const (&kst)[kStages],
+                                        uint16_t* const (&vst)[kStages], const uint16_t* dsr,
+                                        int w4, int lane, float* dq_out, bool rvalid) {
+  constexpr int NMT = D / 32;
+  constexpr int NST = kStages;
+  constexpr int NIW = BlockLoader<D>::NIW;
+  constexpr int DSX = 2 * 64 * 8;
+  const int nblocks = walk.nblocks, nfull = walk.nfull;
+  f32x16 acc[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+  const BlockLoader<D> ldr(w4, lane);
+  // the copies and this wave's MFMAs win ties for issue against the score
+  // wave on the same SIMD (about 3% faster than equal priorities)
+  __builtin_amdgcn_s_setprio(3);
+
+  if (nfull > 0) {
+    constexpr size_t kBlk = (size_t)kBN * D;
+    constexpr unsigned kBlkBytes = kBN * D * 2;
+    // The V copies of loop iteration b (blocks b+3 .. b+6) touch at most two
+    // pages; their slots are looked up one iteration ahead.  A page is looked
+    // up only if a block of it inside the range is copied.
+    int pa_next = walk.page_id(0), pb_next = pa_next;
+    size_t koff[NST];  // source offset of block j, kept from V(j)'s copy to K(j)'s
+    {
+      const size_t p0 = walk.page_base(pa_next);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) koff[j] = j < nfull ? p0 + j * kBlk : 0;
+      // V(0), K(0), V(1), K(1), V(2): the copies of steps -3 .. -1
+      load_block(ldr, vst[0], a.v + koff[0], kBN);
+      load_block(ldr, kst[0], a.k + koff[0], kBN);
+      load_block(ldr, vst[1], a.v + koff[1], kBN);
+      load_block(ldr, kst[1], a.k + koff[1], kBN);
+      load_block(ldr, vst[2], a.v + koff[2], kBN);
+    }
+#define LS_DQ_STEP(ST)                                                                      \
+  if (b + (ST) <= nfull) {                                                                  \
+    /* K(b+ST), V(b+ST) landed; the stages of K(b+ST-2), V(b+ST-1) are free */               \
+    ring_barrier<3 * NIW>();                                                                \
+    constexpr int SK = ((ST) + 2) % NST, SV = ((ST) + 3) % NST;                             \
+    const int jv = b + (ST) + 3;                                                            \
+    const size_t pv = ((jv >> 3) == ((b + 3) >> 3)) ? pa : pb;                              \
+    koff[SV] = jv < nfull ? pv + (jv & 7) * kBlk : 0;                                       \
+    dq_block<D>(tl, ldr, kst[((ST) + 3) % NST], dsr + (((ST) + 1) & 1) * 4 * DSX, acc,      \
+                b + (ST) >= 1, lds_addr(kst[SK]), block_desc(a.k + koff[SK], kBlkBytes),    \
+                lds_addr(vst[SV]), block_desc(a.v + koff[SV], kBlkBytes));                  \
+  }
+    for (int b = 0; b <= nfull; b += NST) {
+      const size_t pa = walk.page_base(pa_next);  // page of block b+3
+      const size_t pb = walk.page_base(pb_next);  // page of block b+6
+      const int ga = b + 7, gb = max(b + 7, ((b + 10) >> 3) << 3);
+      pa_next = ga < nfull ? walk.page_id(ga >> 3) : -1;
+      pb_next = gb < nfull ? walk.page_id(gb >> 3) : -1;
+      LS_DQ_STEP(0)
+      LS_DQ_STEP(1)
+      LS_DQ_STEP(2)
+      LS_DQ_STEP(3)
+    }
+#undef LS_DQ_STEP
+    wait_loads_le<0>();  // drain the look-ahead copies before LDS is reused
+    __syncthreads();
+  }
+
+  // masked blocks (partial last prompt page; the causal response block)
+  for (int j = nfull; j < nblocks; ++j) {
+    int nv, key0;
+    const size_t off = walk.block(j, nv, key0);
+    if (nv > 0) {
+      load_block(ldr, kst[0], a.k + off, nv);
+      load_block(ldr, vst[0], a.v + off, nv);
+    }
+    wait_loads_le<0>();
+    __syncthreads();  // block j's tiles are visible
+    __syncthreads();  // the score waves have stored its dS
+    if (nv > 0) {
+      bf16x8 dsb[2];
+      dsb[0] = *reinterpret_cast<const bf16x8*>(dsr);
+      dsb[1] = *reinterpret_cast<const bf16x8*>(dsr + 64 * 8);
+      block_dq<D>(acc, tl, kst[0], dsb);
+    }
+    __syncthreads();  // tiles and dS are rewritten by the next block
   }
 
   if (rvalid) {
-    const size_t rows_total = (size_t)a.hq * a.R;
-    float* op = a.dq_slots + ((size_t)slot * rows_total + row0 + m) * D + 4 * hf;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
@@ -284,9 +315,69 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dq(const AttnArgs a) {
         v.y = acc[mt][4 * r4 + 1] * a.scale;
         v.z = acc[mt][4 * r4 + 2] * a.scale;
         v.w = acc[mt][4 * r4 + 3] * a.scale;
-        *reinterpret_cast<float4*>(op + 32 * mt + 8 * r4) = v;
+        *reinterpret_cast<float4*>(dq_out + 32 * mt + 8 * r4) = v;
       }
     }
+  }
+}
+
+// dQ of 128 query rows of one KV group over one key range, by two kinds of
+// wave.  Waves 0-3 (score waves) own 32 rows each and hold their Q and dO as
+// MFMA B operands; per key block b they form S(b), dP(b) and dS(b) and store
+// dS(b) to LDS.  Waves 4-7 (dQ waves) own the same rows one to one, hold the
+// dQ^T accumulators, and one block behind accumulate K(b-1)^T dS(b-1); they
+// also issue every K/V copy.  With 512 threads a SIMD runs two waves, normally
+// one of each kind, so the score wave's exp/VALU work and its waits overlap the
+// dQ wave's MFMAs instead of idling the matrix unit; each kind needs half the
+// registers of a wave that does both.
+//
+// Ring (four K stages, four V stages; block j in stage j % 4): step b starts
+// with one barrier, after which K(b), V(b) have landed; the score waves read
+// K(b), V(b), the dQ waves K(b-1), and the dQ waves copy K(b+2) and V(b+3)
+// into the stages of K(b-2) and V(b-1), both last read before that barrier.
+// Per step every dQ wave issues the same copies (blocks past the range
+// re-read block 0), so each wait is a fixed vmcnt: K(b) was issued two steps
+// and V(b) three steps before step b, and only V(b+1), K(b+1), V(b+2) may
+// still be in flight.  dS goes through two LDS buffers (dS(b) in buffer
+// b % 2).  Step nfull only drains the last dQ.
+template <int D, bool RESP>
+__global__ void __launch_bounds__(512, 1) k_bwd_dq(const AttnArgs a) {
+  constexpr int TILE = kBN * D;
+  constexpr int DSX = 2 * 64 * 8;  // elements of one wave's dS^T block
+  static_assert(kStages == 4, "the ring has four stages");
+  // one array per ring stage (distinct LDS objects; see the forward kernel)
+  __shared__ __attribute__((aligned(1024))) uint16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t dsx[2 * 4 * DSX];  // [buffer][wave][ks][lane][8]
+  uint16_t* const kst[kStages] = {k0, k1, k2, k3};
+  uint16_t* const vst[kStages] = {v0, v1, v2, v3};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w4 = wave & 3;
+  const int hf = lane >> 5, lq = lane & 31;
+
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_unit = a.mtiles * a.hkv;
+  const int unit = w / per_unit;
+  const int rem = w - unit * per_unit;
+  const int kv = rem / a.mtiles;
+  const int mtile = rem - kv * a.mtiles;
+  const int GR = (a.hq / a.hkv) * a.R;
+  const int m0 = mtile * kBwdRows;
+  const int m = m0 + 32 * w4 + lq;
+  const bool rvalid = m < GR;
+  const size_t row0 = (size_t)kv * GR;
+
+  const KeyWalk<D, RESP> walk(a, kv, unit, m0, kBwdRows);
+  const Lanes32<D> tl(hf, lq);
+  uint16_t* const ds_lane = dsx + w4 * DSX + lane * 8;  // this lane's dS^T, buffer 0
+  if (wave < 4) {
+    score_role<D, RESP>(a, walk, tl, kst, vst, ds_lane, row0 + min(m, GR - 1), rvalid, m % a.R, hf);
+  } else {
+    const size_t rows_total = (size_t)a.hq * a.R;
+    float* op = a.dq_slots + ((size_t)(a.slot_base + unit) * rows_total + row0 + m) * D + 4 * hf;
+    dq_role<D, RESP>(a, walk, tl, kst, vst, ds_lane, w4, lane, op, rvalid);
   }
 }
 
@@ -405,7 +496,7 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  dim3 g(grid), b(256);
+  dim3 g(grid), b(512);
   if (head_dim == 256) {
     if (resp) hipLaunchKernelGGL((k_bwd_dq<256, true>), g, b, 0, s, a);
     else hipLaunchKernelGGL((k_bwd_dq<256, false>), g, b, 0, s, a);

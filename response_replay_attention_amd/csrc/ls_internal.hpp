@@ -13,7 +13,7 @@ constexpr int kPage = 256;       // prompt tokens per page (only size supported)
 constexpr int kBN = 32;          // keys per inner block (one 32-row MFMA tile)
 constexpr int kFwdWaves = 8;     // waves per forward workgroup (two per SIMD)
 constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per forward workgroup (32 per wave)
-constexpr int kBwdRows = 128;    // query rows per dQ workgroup (4 waves x 32)
+constexpr int kBwdRows = 128;    // query rows per dQ workgroup (4 score + 4 dQ waves, 32 rows each)
 constexpr int kTargetWGs = 256;  // one workgroup per CU on MI355X (256 CUs)
 constexpr int kMaxChunks = 64;   // cap on internal sub-splits per split
 constexpr int kStages = 4;       // LDS ring depth of K/V blocks in the key loops
