@@ -313,8 +313,8 @@ def main() -> int:
 
     import torch
 
-    from replay_inputs import (CAPTURE_WORKLOADS, GROUP_2M, GROUP_2M_RESP_LENS, WORKLOADS,
-                               make_inputs, make_response)
+    from replay_inputs import (CAPTURE_WORKLOADS, FULL_2M, GROUP_2M, GROUP_2M_RESP_LENS,
+                               WORKLOADS, make_inputs, make_response)
     if args.workload in CAPTURE_WORKLOADS:
         return bench_capture(args, CAPTURE_WORKLOADS[args.workload])
     from response_replay_attention_amd import (Member, PromptCache, block_bounds, ls_timing_enable,
@@ -404,7 +404,9 @@ def main() -> int:
         dom_flops /= len(block_inputs)
     achieved = dom_flops / (dom["avg_ms"] * 1e-3) / 1e12
     digest = source_digest()
-    traffic = None if args.score else read_traffic(digest)
+    # the counters were taken on the default workload (random page placement)
+    traffic = (read_traffic(digest) if shape.name == FULL_2M.name and not args.score
+               and not args.identity_pages and not block_inputs else None)
 
     out = {
         "metric": "replay-attn fwd+bwd TFLOP/s & prompt-keys/s at 2M prefix; % bf16 MFMA peak",
