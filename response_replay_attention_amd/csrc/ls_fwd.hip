@@ -67,6 +67,9 @@ __device__ __forceinline__ void fwd_step(const LanesCM<D>& tl, const BlockLoader
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  // the score MFMAs form one dependent chain; they win issue ties against the
+  // other wave's PV MFMAs (about 3 % faster than equal priorities)
+  __builtin_amdgcn_s_setprio(2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -79,6 +82,7 @@ __device__ __forceinline__ void fwd_step(const LanesCM<D>& tl, const BlockLoader
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
   if (MASK) {
     // key crow(r, hf) = 4*hf + 8*(r/4) + r%4 of the block is visible iff
     // kmin <= key <= min(nvalid - 1, kmax); compared as compile-time row
