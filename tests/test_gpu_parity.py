@@ -24,6 +24,7 @@ SMALL = [
     ReplayShape("empty_splits", 6, 1, 128, 4 * 256, 64, 6),
     ReplayShape("chunked_single_split", 6, 1, 128, 64 * 256, 128, 1),
     ReplayShape("gqa24x4_d256_p4096_r256_s8", 24, 4, 256, 16 * 256, 256, 8),
+    ReplayShape("partial_page_only_d256", 24, 4, 256, 100, 70, 2, extra_phys_pages=1),
 ]
 
 
