@@ -382,97 +382,156 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dq(const AttnArgs a) {
 }
 
 // dK or dV of 32 response keys [j0, j0+32) of KV head kv from the query head
-// kv*g + blockIdx.z, one wave per workgroup, key-stationary: loops over the
-// query rows i of that head that see the keys (qoff + i >= j0, in blocks of
-// 32 from i = max(0, j0 - qoff)), accumulating
+// kv*g + hh, by one wave, key-stationary: loops over the query rows i of that
+// head that see the keys (qoff + i >= j0, in blocks of 32 from
+// i = max(0, j0 - qoff)), accumulating
 //   DV:  dV^T[d][key] += sum_query dO[query][d] P[query][key]
 //   DK:  dK^T[d][key] += sum_query Q[query][d]  dS[query][key]
 // with S = Q K^T and dP = dO V^T recomputed in the (query x key) orientation.
-// Each head writes its own fp32 partial (k_kv_reduce sums the g heads of a
-// group in head order), so the launch has g times more workgroups than key
-// blocks and needs no atomics.  dV and dK are separate launches so each needs
-// only one 128-register accumulator set.
+// The key block's K (and V) rows stay in registers as the B operands of S (and
+// dP).  The Q and dO tiles of query block t+1 are copied into the second of two
+// LDS buffers while block t is computed, and every LDS operand is read four
+// MFMAs ahead of its use (fenced, as in the prompt kernels); one wait per block
+// (ring_barrier) hands the buffers over.  Each head writes its own fp32 partial
+// (k_kv_reduce sums the g heads of a group in head order), so no atomics are
+// needed.
 template <int D, bool DK>
-__global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
+__device__ __forceinline__ void resp_kv_wave(const AttnArgs& a, int kv, int hh, int j0,
+                                             uint16_t* smem, float (&s_lse2)[2][kBN],
+                                             float (&s_dval)[2][kBN], int lane) {
   constexpr int NKK = D / 16;
   constexpr int NMT = D / 32;
   constexpr int TILE = kBN * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // K_r, V_r, Q, dO
-  __shared__ float s_lse2[kBN], s_dval[kBN];
-
-  const int lane = threadIdx.x, hf = lane >> 5, lq = lane & 31;
-  const int kv = blockIdx.y;
-  const int hh = blockIdx.z;  // query head within the group
-  const int j0 = blockIdx.x * kBN;
+  constexpr int PF = 4;             // LDS prefetch distance, in MFMAs
+  constexpr int NA = DK ? 2 * NKK : NKK;  // S (and dP) MFMAs per block, two chains
+  constexpr int NC = 2 * NMT;       // accumulation MFMAs per block
+  const int hf = lane >> 5, lq = lane & 31;
   const int g = a.hq / a.hkv;
-  uint16_t* kt = smem;
-  uint16_t* vt = smem + TILE;
-  uint16_t* qt = smem + 2 * TILE;
-  uint16_t* dt = smem + 3 * TILE;
+  // Four tiles: Q of buffer b at smem + b TILE, dO of buffer b at
+  // smem + (2 + b) TILE (offsets from the one LDS array, so every access stays
+  // an LDS access).  K_r and V_r pass through buffer 1's tiles on their way to
+  // registers, before block 1 is copied there.
+  const BlockLoader<D, 1> ldr(0, lane);
+  const Lanes32<D> tl(hf, lq);
 
   const int nkeys = min(kBN, a.RK - j0);
   {
     const size_t off = ((size_t)kv * a.kvr + j0) * D;
-    tile_load_async<D, 1>(kt, a.k + off, nkeys, 0, lane);
-    if (DK) tile_load_async<D, 1>(vt, a.v + off, nkeys, 0, lane);
+    load_block(ldr, smem + TILE, a.k + off, nkeys);
+    if (DK) load_block(ldr, smem + 3 * TILE, a.v + off, nkeys);
   }
-  const Lanes32<D> tl(hf, lq);
-  const int key = j0 + lq;  // this lane's key column
+  const int h = kv * g + hh;
+  const int ib = max(0, j0 - a.qoff);                  // first query row of the loop
+  const int nblk = ib < a.R ? (a.R - ib + kBN - 1) / kBN : 0;
+  // Q, dO tiles of block t into buffer t & 1; this lane's LSE*log2(e) and D
+  // (query ib + 32t + lane, lanes < 32) into registers, stored after the wait
+  auto issue = [&](int t, float& l2, float& dv) {
+    const int i0 = ib + t * kBN, nq = min(kBN, a.R - i0);
+    const bool ok = lane < nq;
+    const size_t r = (size_t)h * a.R + i0 + (ok ? lane : 0);
+    l2 = ok ? a.lse[r] * kLog2e : kInf;
+    dv = ok ? a.dvals[r] : 0.f;
+    const size_t qo = ((size_t)h * a.R + i0) * D;
+    load_block(ldr, smem + (t & 1) * TILE, a.q + qo, nq);
+    load_block(ldr, smem + (2 + (t & 1)) * TILE, a.d_o + qo, nq);
+  };
 
+  float l2n = kInf, dvn = 0.f;
+  if (nblk > 0) issue(0, l2n, dvn);
+  ring_barrier<0>();  // K_r (V_r) and block 0 have landed
+  bf16x8 kr[NKK], vr[DK ? NKK : 1];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    kr[kk] = tl.row8(smem + TILE, kk);
+    if (DK) vr[kk] = tl.row8(smem + 3 * TILE, kk);
+  }
+  if (lane < kBN) {
+    s_lse2[0][lane] = l2n;
+    s_dval[0][lane] = dvn;
+  }
+  ring_barrier<0>();  // the K_r / V_r reads have returned: buffer 1 is free
+
+  const int key = j0 + lq;  // this lane's key column
   f32x16 acc[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
-  {
-    const int h = kv * g + hh;
-    for (int i0 = max(0, j0 - a.qoff); i0 < a.R; i0 += kBN) {
-      const int nq = min(kBN, a.R - i0);
-      const size_t qoff = ((size_t)h * a.R + i0) * D;
-      __syncthreads();  // previous block's reads of qt/dt and s_* are done
-      tile_load_async<D, 1>(qt, a.q + qoff, nq, 0, lane);
-      tile_load_async<D, 1>(dt, a.d_o + qoff, nq, 0, lane);
-      if (lane < kBN) {
-        const bool ok = lane < nq;
-        const size_t r = (size_t)h * a.R + i0 + (ok ? lane : 0);
-        s_lse2[lane] = ok ? a.lse[r] * kLog2e : kInf;
-        s_dval[lane] = ok ? a.dvals[r] : 0.f;
-      }
-      wait_async_loads();
-      __syncthreads();
+  for (int t = 0; t < nblk; ++t) {
+    const int cb = t & 1;
+    if (t + 1 < nblk) issue(t + 1, l2n, dvn);
+    const int i0 = ib + t * kBN, nq = min(kBN, a.R - i0);
+    const uint16_t* q = smem + cb * TILE;
+    const uint16_t* d_o = smem + (2 + cb) * TILE;
+    // this lane's 16 queries crow(r, hf) = 8*(r/4) + 4*hf + r%4: four runs of 4
+    f32x4 lse4[4], dv4[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      lse4[r4] = *reinterpret_cast<const f32x4*>(&s_lse2[cb][8 * r4 + 4 * hf]);
+      if (DK) dv4[r4] = *reinterpret_cast<const f32x4*>(&s_dval[cb][8 * r4 + 4 * hf]);
+    }
 
-      // S[query][key] = sum_d Q[query][d] K[key][d]; dP likewise with dO, V
-      f32x16 s, dp;
+    // S[query][key] = sum_d Q[query][d] K[key][d] (DV: two chains over even and
+    // odd k-steps; DK: one chain, interleaved with dP = dO V^T)
+    auto aop = [&](int i) -> bf16x8 {
+      if (DK) return (i & 1) ? tl.row8(d_o, i >> 1) : tl.row8(q, i >> 1);
+      return tl.row8(q, i >> 1 | (i & 1) * (NKK / 2));
+    };
+    bf16x8 rf[NA];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
+    for (int i = 0; i < PF; ++i) rf[i] = aop(i);
+    f32x16 s0, s1;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s = mfma32(tl.row8(qt, kk), tl.row8(kt, kk), s);
-        if (DK) dp = mfma32(tl.row8(dt, kk), tl.row8(vt, kk), dp);
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      if (DK) {
+        if (i & 1) s1 = mfma32(rf[i], vr[i >> 1], s1);
+        else s0 = mfma32(rf[i], kr[i >> 1], s0);
+      } else {
+        const int kk = i >> 1 | (i & 1) * (NKK / 2);
+        if (i & 1) s1 = mfma32(rf[i], kr[kk], s1);
+        else s0 = mfma32(rf[i], kr[kk], s0);
       }
+      if (i + PF < NA) rf[i + PF] = aop(i + PF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // X^T operand of the accumulation (dO^T for dV, Q^T for dK), first reads
+    const uint16_t* xt = DK ? q : d_o;
+    bf16x8 cf[NC];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) cf[j] = tl.col8(xt, j / NMT, j % NMT);
 
-      // P (or dS) as the B operand: register 8*ks + e holds query kperm(ks,hf,e)
-      bf16x8 pb[2];
+    // P (or dS) as the B operand: register 8*ks + e holds query kperm(ks,hf,e)
+    bf16x8 pb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = crow(r, hf);
-        const bool ok = (q < nq) && (key < a.RK) && (key <= a.qoff + i0 + q);
-        const float p = ok ? __builtin_amdgcn_exp2f(s[r] * a.s2 - s_lse2[q]) : 0.f;
-        const float val = DK ? p * (dp[r] - s_dval[q]) : p;
-        pb[r >> 3][r & 7] = to_bf16(val);
-      }
+    for (int r = 0; r < 16; ++r) {
+      // masked scores enter the exponential as -inf (P = 0): no branch
+      const int qr = crow(r, hf);
+      const bool ok = (qr < nq) & (key < a.RK) & (key <= a.qoff + i0 + qr);
+      const float sc = ok ? (DK ? s0[r] : s0[r] + s1[r]) : -kInf;
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc, a.s2, -lse4[r >> 2][r & 3]));
+      pb[r >> 3][r & 7] = to_bf16(DK ? p * (s1[r] - dv4[r >> 2][r & 3]) : p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-      // dV^T (or dK^T)[d][key] += sum_query X^T[d][query] pb[query][key]
-      const uint16_t* xt = DK ? qt : dt;
+    // dV^T (or dK^T)[d][key] += sum_query X^T[d][query] pb[query][key]
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma32(tl.col8(xt, ks, mt), pb[ks], acc[mt]);
-      }
+    for (int j = 0; j < NC; ++j) {
+      acc[j % NMT] = mfma32(cf[j], pb[j / NMT], acc[j % NMT]);
+      if (j + PF < NC) cf[j + PF] = tl.col8(xt, (j + PF) / NMT, (j + PF) % NMT);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // block t+1 has landed and every read of buffer cb has returned
+    ring_barrier<0>();
+    if (t + 1 < nblk && lane < kBN) {
+      s_lse2[cb ^ 1][lane] = l2n;
+      s_dval[cb ^ 1][lane] = dvn;
     }
   }
 
@@ -494,6 +553,21 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
   }
 }
 
+// Response dV and dK in one launch: grid (key blocks, Hkv, 2g), z < g the dV
+// partial of query head z, z >= g the dK partial of query head z - g, so the
+// two kinds run side by side instead of one after the other.  64 KiB of LDS per
+// workgroup: two workgroups per CU.
+template <int D>
+__global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
+  constexpr int TILE = kBN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // Q x2, dO x2
+  __shared__ __attribute__((aligned(16))) float s_lse2[2][kBN], s_dval[2][kBN];
+  const int g = a.hq / a.hkv;
+  const int z = blockIdx.z;
+  if (z < g) resp_kv_wave<D, false>(a, blockIdx.y, z, blockIdx.x * kBN, smem, s_lse2, s_dval, threadIdx.x);
+  else resp_kv_wave<D, true>(a, blockIdx.y, z - g, blockIdx.x * kBN, smem, s_lse2, s_dval, threadIdx.x);
+}
+
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   dim3 g(grid), b(512);
@@ -508,14 +582,9 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, h
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s) {
-  dim3 g((a.RK + kBN - 1) / kBN, a.hkv, a.hq / a.hkv), b(64);
-  if (head_dim == 256) {
-    hipLaunchKernelGGL((k_bwd_resp_kv<256, false>), g, b, 0, s, a);
-    hipLaunchKernelGGL((k_bwd_resp_kv<256, true>), g, b, 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_bwd_resp_kv<128, false>), g, b, 0, s, a);
-    hipLaunchKernelGGL((k_bwd_resp_kv<128, true>), g, b, 0, s, a);
-  }
+  dim3 g((a.RK + kBN - 1) / kBN, a.hkv, 2 * (a.hq / a.hkv)), b(64);
+  if (head_dim == 256) hipLaunchKernelGGL((k_bwd_resp_kv<256>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((k_bwd_resp_kv<128>), g, b, 0, s, a);
   return hipGetLastError();
 }
 
