@@ -553,9 +553,11 @@ __device__ __forceinline__ void resp_kv_wave(const AttnArgs& a, int kv, int hh, 
   }
 }
 
-// Response dV and dK in one launch: grid (key blocks, Hkv, 2g), z < g the dV
-// partial of query head z, z >= g the dK partial of query head z - g, so the
-// two kinds run side by side instead of one after the other.  64 KiB of LDS per
+// Response dV and dK in one launch, one work item per (KV head, query head of
+// the group, kind, key block), key block fastest: the dV and dK partials run
+// side by side instead of one launch after the other.  Work items are dealt to
+// the XCDs in contiguous ranges, so the items of a query head -- which all copy
+// that head's Q and dO tiles -- share one XCD's L2.  64 KiB of LDS per
 // workgroup: two workgroups per CU.
 template <int D>
 __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
@@ -563,9 +565,15 @@ __global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // Q x2, dO x2
   __shared__ __attribute__((aligned(16))) float s_lse2[2][kBN], s_dval[2][kBN];
   const int g = a.hq / a.hkv;
-  const int z = blockIdx.z;
-  if (z < g) resp_kv_wave<D, false>(a, blockIdx.y, z, blockIdx.x * kBN, smem, s_lse2, s_dval, threadIdx.x);
-  else resp_kv_wave<D, true>(a, blockIdx.y, z - g, blockIdx.x * kBN, smem, s_lse2, s_dval, threadIdx.x);
+  const int nkb = (a.RK + kBN - 1) / kBN;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = w % nkb;
+  const int rest = w / nkb;
+  const int dk = rest & 1;
+  const int hh = (rest >> 1) % g;
+  const int kv = (rest >> 1) / g;
+  if (!dk) resp_kv_wave<D, false>(a, kv, hh, kb * kBN, smem, s_lse2, s_dval, threadIdx.x);
+  else resp_kv_wave<D, true>(a, kv, hh, kb * kBN, smem, s_lse2, s_dval, threadIdx.x);
 }
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s) {
@@ -582,7 +590,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, h
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s) {
-  dim3 g((a.RK + kBN - 1) / kBN, a.hkv, 2 * (a.hq / a.hkv)), b(64);
+  dim3 g(((a.RK + kBN - 1) / kBN) * a.hkv * 2 * (a.hq / a.hkv)), b(64);
   if (head_dim == 256) hipLaunchKernelGGL((k_bwd_resp_kv<256>), g, b, 0, s, a);
   else hipLaunchKernelGGL((k_bwd_resp_kv<128>), g, b, 0, s, a);
   return hipGetLastError();
