@@ -80,7 +80,7 @@ __device__ __forceinline__ void score_block(const Lanes32<D>& tl, const uint16_t
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     s[r] = 0.f;
-    dp[r] = 0.f;
+    dp[r] = -dval;  // the accumulation starts at -D: it ends at dP - D
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -97,7 +97,7 @@ __device__ __forceinline__ void score_block(const Lanes32<D>& tl, const uint16_t
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], s2, -lse2));
-    dsb[r >> 3][r & 7] = to_bf16(p * (dp[r] - dval));
+    dsb[r >> 3][r & 7] = to_bf16(p * dp[r]);
   }
   *reinterpret_cast<bf16x8*>(dsw) = dsb[0];
   *reinterpret_cast<bf16x8*>(dsw + 64 * 8) = dsb[1];
