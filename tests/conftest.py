@@ -11,9 +11,3 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size case (minutes of host time)")
-
-
-def pytest_collection_modifyitems(config, items):
-    # a GPU test on a machine without a GPU is a configuration error, not a skip:
-    # the driver runs `-m gpu` only on the GPU machine.
-    pass
