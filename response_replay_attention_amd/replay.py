@@ -47,6 +47,17 @@ def _on_stream(fn):
     return wrapped
 
 
+def _upload(arr, dev: torch.device) -> torch.Tensor:
+    """A host int32 array on ``dev`` without a host synchronisation: staged
+    through pinned memory and copied on the current stream (a plain copy from
+    pageable memory waits for all earlier work on the stream, which leaves the
+    GPU idle while the host prepares the next launches)."""
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if dev.type != "cuda":
+        return t.to(dev)
+    return t.pin_memory().to(dev, non_blocking=True)
+
+
 class PromptCache:
     """A detached prompt: bf16 K/V pools ``[num_phys, Hkv, 256, d]`` (never
     written by this package) and the page table that maps its logical pages to
@@ -73,14 +84,31 @@ class PromptCache:
         self.l2p = l2p_np
         self.order = order
         self.split_offsets_host = np.ascontiguousarray(offs)  # kept alive: the table points at it
-        self._l2p_dev = torch.from_numpy(np.ascontiguousarray(l2p_np)).to(dev)
-        self._order_dev = torch.from_numpy(np.ascontiguousarray(order)).to(dev)
-        self._offs_dev = torch.from_numpy(self.split_offsets_host.copy()).to(dev)
+        self._l2p_dev = _upload(l2p_np, dev)
+        self._order_dev = _upload(order, dev)
+        self._offs_dev = _upload(self.split_offsets_host.copy(), dev)
+        # the uploads run on the stream current here; table() orders the
+        # stream a driver runs on after them
+        self._ready = None
+        if dev.type == "cuda":
+            self._ready = torch.cuda.Event()
+            self._ready.record(torch.cuda.current_stream(dev))
         self.pt = B.PageTable(
             self._l2p_dev.data_ptr() if self.num_pages else 0,
             self._order_dev.data_ptr() if self.num_pages else 0,
             self._offs_dev.data_ptr(), self.split_offsets_host.ctypes.data,
             self.num_pages, self.num_splits, self.num_phys)
+
+    def table(self) -> "B.PageTable":
+        """The page table for a launch on the current stream: the stream waits
+        for the table's upload, and the table's device buffers are marked as
+        used by it (so the caching allocator keeps them until its work is done)."""
+        if self._ready is not None:
+            s = torch.cuda.current_stream(self.k_pool.device)
+            s.wait_event(self._ready)
+            for t in (self._l2p_dev, self._order_dev, self._offs_dev):
+                t.record_stream(s)
+        return self.pt
 
     def shape(self, q: torch.Tensor, scale: Optional[float] = None, q_offset: int = 0,
               kv_rows: int = 0, flags: int = 0) -> B.AttnShape:
@@ -117,7 +145,7 @@ def replay_forward(cache: PromptCache, q, k_resp, v_resp, scale=None, stream=Non
     part_l = torch.empty(nparts, hq, r, dtype=torch.float32, device=dev)
     wsb = B.ls_replay_attn_fwd_workspace(sh, cache.pt)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
-    B.ls_replay_attn_fwd(sh, cache.pt, q, cache.k_pool, cache.v_pool, k_resp, v_resp,
+    B.ls_replay_attn_fwd(sh, cache.table(), q, cache.k_pool, cache.v_pool, k_resp, v_resp,
                          part_o, part_m, part_l, ws, stream)
     o = torch.empty(hq, r, d, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(hq, r, dtype=torch.float32, device=dev)
@@ -150,8 +178,8 @@ def score_group(cache: PromptCache, members: Iterable["Member"], scale=None, str
     part_l = torch.empty(nparts, hq, r, dtype=torch.float32, device=dev)
     wsb = B.ls_replay_attn_fwd_workspace(sh, cache.pt)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
-    offs_dev = torch.from_numpy(offs).to(dev) if len(members) > 1 else None
-    B.ls_replay_attn_fwd_members(sh, cache.pt, offs, offs_dev, q, cache.k_pool, cache.v_pool,
+    offs_dev = _upload(offs, dev) if len(members) > 1 else None
+    B.ls_replay_attn_fwd_members(sh, cache.table(), offs, offs_dev, q, cache.k_pool, cache.v_pool,
                                  k_resp, v_resp, part_o, part_m, part_l, ws, stream)
     o = torch.empty(hq, r, d, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(hq, r, dtype=torch.float32, device=dev)
@@ -185,7 +213,7 @@ def replay_backward(cache: PromptCache, q, k_resp, v_resp, o, lse, d_o, scale=No
             dv[:, q_offset + r:].zero_()
     wsb = B.ls_replay_attn_bwd_workspace(sh, cache.pt)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    B.ls_replay_attn_bwd(sh, cache.pt, q, cache.k_pool, cache.v_pool, k_resp, v_resp, o, lse, d_o,
+    B.ls_replay_attn_bwd(sh, cache.table(), q, cache.k_pool, cache.v_pool, k_resp, v_resp, o, lse, d_o,
                          dq, dk, dv, ws, stream)
     del ws
     return dq, dk, dv
@@ -259,7 +287,7 @@ def capture_prefill(chunks: Iterable, k_pool: torch.Tensor, v_pool: torch.Tensor
     if slots_np.size and (slots_np.min() < 0 or slots_np.max() >= num_phys):
         raise ValueError("slots must lie in [0, num_phys_pages)")
     dev = k_pool.device
-    slots_dev = torch.from_numpy(slots_np.copy()).to(dev)
+    slots_dev = _upload(slots_np.copy(), dev)
     outputs: List = []
     c0 = 0
     for i, (q, k, v) in enumerate(chunks):
