@@ -25,43 +25,55 @@ __global__ void __launch_bounds__(256) k_merge(int nper, int64_t rows, const flo
   if (row >= rows) return;
   const int c0 = grp * nper;
 
-  float big = -kInf;
-  for (int c = 0; c < nper; ++c) {
-    const size_t i = (size_t)(c0 + c) * rows + row;
-    if (pl[i] > 0.f) big = fmaxf(big, pm[i]);
-  }
-  float tot = 0.f;
+  // Parts are taken in batches of NB whose loads are all issued together (one
+  // memory phase per batch).  Within a batch the weights are l_c e^{m_c - big}
+  // with big the running maximum of m over the non-empty parts so far; when a
+  // batch raises it, what was summed before is rescaled.  Parts are added in
+  // index order; a part whose weight is 0 (empty, or underflowed) adds
+  // nothing.  With at most NB parts this is the two-pass formula with the
+  // global maximum, term for term.
+  constexpr int NB = 12;
+  float big = -kInf, tot = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // parts are added in index order; four parts' loads are issued together
-  // (an empty part has l = 0 and o = 0, so it adds exactly nothing)
-  auto add = [&](const float4& o, float w) {
-    tot += w;
-    acc.x += w * o.x;
-    acc.y += w * o.y;
-    acc.z += w * o.z;
-    acc.w += w * o.w;
-  };
-  if (big != -kInf) {
-    int c = 0;
-    for (; c + 4 <= nper; c += 4) {
-      float4 o[4];
-      float w[4];
+  for (int cb = 0; cb < nper; cb += NB) {
+    float4 o[NB];
+    float m[NB], l[NB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const size_t i = (size_t)(c0 + c + u) * rows + row;
+    for (int u = 0; u < NB; ++u) {
+      if (cb + u < nper) {
+        const size_t i = (size_t)(c0 + cb + u) * rows + row;
         o[u] = *reinterpret_cast<const float4*>(po + i * D + 4 * e4);
-        const float l = pl[i];
-        w[u] = l > 0.f ? l * expf(pm[i] - big) : 0.f;
+        m[u] = pm[i];
+        l[u] = pl[i];
+      } else {
+        l[u] = 0.f;
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (w[u] > 0.f) add(o[u], w[u]);
     }
-    for (; c < nper; ++c) {
-      const size_t i = (size_t)(c0 + c) * rows + row;
-      const float l = pl[i];
-      if (!(l > 0.f)) continue;
-      add(*reinterpret_cast<const float4*>(po + i * D + 4 * e4), l * expf(pm[i] - big));
+    float bm = big;
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (l[u] > 0.f) bm = fmaxf(bm, m[u]);
+    if (bm > big) {
+      if (big != -kInf) {
+        const float r = expf(big - bm);
+        tot *= r;
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
+      }
+      big = bm;
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const float w = l[u] > 0.f ? l[u] * expf(m[u] - big) : 0.f;
+      if (w > 0.f) {
+        tot += w;
+        acc.x += w * o[u].x;
+        acc.y += w * o[u].y;
+        acc.z += w * o[u].z;
+        acc.w += w * o[u].w;
+      }
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
