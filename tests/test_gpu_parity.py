@@ -179,6 +179,22 @@ def test_split_policy_invariance():
         assert_close("dQ vs S=1", dq, results[0][2])
 
 
+def test_merge_of_many_full_parts():
+    """More parts than the merge loads at once (12): a 16-page prompt dealt to
+    16 and 24 splits gives 17 and 25 parts that hold keys (plus empty ones), so
+    rows whose maximum sits in a later batch rescale what the earlier batches
+    summed.  Checked against the oracle and against one split."""
+    shape = SMALL[6]
+    inp = make_inputs(shape, seed=13, device="cuda")
+    _, ref, dq1, _, _ = run_hip(shape, inp, num_splits=1)
+    for ns, pol in ((16, SPLIT_CONTIGUOUS), (24, SPLIT_BLOCK_CYCLIC)):
+        _, fwd, dq, dk, dv = run_hip(shape, inp, num_splits=ns, policy=pol, block_pages=1)
+        check_all(shape, inp, fwd, dq, dk, dv)
+        assert_close("O vs S=1", fwd.o.float(), ref.o.float())
+        assert_lse_close("LSE vs S=1", fwd.lse, ref.lse)
+        assert_close("dQ vs S=1", dq, dq1)
+
+
 def test_page_placement_does_not_change_bits():
     """The same logical prompt under the identity map and under a random map
     gives bitwise identical outputs: the page table only changes addresses."""
