@@ -244,12 +244,15 @@ __device__ __forceinline__ void dq_role(const AttnArgs& a, const KeyWalk<D, RESP
     // The V copies of loop iteration b (blocks b+3 .. b+6) touch at most two
     // pages; their slots are looked up one iteration ahead.  A page is looked
     // up only if a block of it inside the range is copied.
-    int pa_next = walk.page_id(0), pb_next = pa_next;
+    // (response keys are contiguous: block j is rows [32j, 32j+32) of this KV head)
+    int pa_next = RESP ? -1 : walk.page_id(0), pb_next = pa_next;
     size_t koff[NST];  // source offset of block j, kept from V(j)'s copy to K(j)'s
     {
-      const size_t p0 = walk.page_base(pa_next);
+      const size_t p0 = RESP ? 0 : walk.page_base(pa_next);
 #pragma unroll
-      for (int j = 0; j < 3; ++j) koff[j] = j < nfull ? p0 + j * kBlk : 0;
+      for (int j = 0; j < 3; ++j)
+        koff[j] = j < nfull ? (RESP ? ((size_t)walk.kv * a.kvr + (size_t)j * kBN) * D : p0 + j * kBlk)
+                            : 0;
       // V(0), K(0), V(1), K(1), V(2): the copies of steps -3 .. -1
       load_block(ldr, vst[0], a.v + koff[0], kBN);
       load_block(ldr, kst[0], a.k + koff[0], kBN);
@@ -264,17 +267,19 @@ __device__ __forceinline__ void dq_role(const AttnArgs& a, const KeyWalk<D, RESP
     constexpr int SK = ((ST) + 2) % NST, SV = ((ST) + 3) % NST;                             \
     const int jv = b + (ST) + 3;                                                            \
     const size_t pv = ((jv >> 3) == ((b + 3) >> 3)) ? pa : pb;                              \
-    koff[SV] = jv < nfull ? pv + (jv & 7) * kBlk : 0;                                       \
+    koff[SV] = jv >= nfull ? 0                                                              \
+               : RESP ? ((size_t)walk.kv * a.kvr + (size_t)jv * kBN) * D                    \
+                      : pv + (jv & 7) * kBlk;                                               \
     dq_block<D>(tl, ldr, kst[((ST) + 3) % NST], dsr + (((ST) + 1) & 1) * 4 * DSX, acc,      \
                 b + (ST) >= 1, lds_addr(kst[SK]), block_desc(a.k + koff[SK], kBlkBytes),    \
                 lds_addr(vst[SV]), block_desc(a.v + koff[SV], kBlkBytes));                  \
   }
     for (int b = 0; b <= nfull; b += NST) {
-      const size_t pa = walk.page_base(pa_next);  // page of block b+3
-      const size_t pb = walk.page_base(pb_next);  // page of block b+6
+      const size_t pa = RESP ? 0 : walk.page_base(pa_next);  // page of block b+3
+      const size_t pb = RESP ? 0 : walk.page_base(pb_next);  // page of block b+6
       const int ga = b + 7, gb = max(b + 7, ((b + 10) >> 3) << 3);
-      pa_next = ga < nfull ? walk.page_id(ga >> 3) : -1;
-      pb_next = gb < nfull ? walk.page_id(gb >> 3) : -1;
+      pa_next = (!RESP && ga < nfull) ? walk.page_id(ga >> 3) : -1;
+      pb_next = (!RESP && gb < nfull) ? walk.page_id(gb >> 3) : -1;
       LS_DQ_STEP(0)
       LS_DQ_STEP(1)
       LS_DQ_STEP(2)

@@ -372,7 +372,10 @@ struct KeyWalk {
       const int imax = one_head ? mlast % a.R : a.R - 1;
       nblocks = (a.qoff + imax + kBN) / kBN;
       jfirst = one_head ? member_start(a, m0 % a.R) / kBN : 0;
-      nfull = 0;
+      // in the response of one member, when the tile stays in one query head,
+      // the keys that even its first row sees need no mask: they stream
+      // through the ring like prompt blocks
+      nfull = (one_head && !a.moffs) ? min((a.qoff + m0 % a.R + 1) / kBN, nblocks) : 0;
     } else {
       const int c = unit / a.chunks, k = unit - c * a.chunks;
       int s0 = ld_table(a.offs, c), s1 = ld_table(a.offs, c + 1);

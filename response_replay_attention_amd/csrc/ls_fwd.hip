@@ -157,13 +157,8 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   const int nblocks = walk.nblocks;
   // leading blocks that need no mask: the full prompt pages of the range or,
   // in the response block of one response when the tile stays in one query
-  // head, the keys that even the tile's first row sees (these then stream
-  // through the ring like prompt blocks)
-  int nfull = walk.nfull;
-  if (RESP && !a.moffs) {
-    const int mlast = min(m0 + kFwdRows, GR) - 1;
-    if (m0 / a.R == mlast / a.R) nfull = min((a.qoff + m0 % a.R + 1) / kBN, nblocks);
-  }
+  // head, the keys that even the tile's first row sees (KeyWalk)
+  const int nfull = walk.nfull;
   const int slot = a.slot_base + unit;
 
   // Q (B operand): column = query m, k = 16*kk + 8*hf + e.  Rows past the
