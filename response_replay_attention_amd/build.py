@@ -36,9 +36,17 @@ def _hipcc() -> str:
     return "hipcc"
 
 
+# Per-source additions.  ls_bwd.hip: MFMA results in VGPR form.  The response
+# dK/dV kernel needs more than 256 registers per wave; left to choose, the
+# compiler keeps its accumulators in AGPRs and copies values between the two
+# register files around every block (hundreds of moves per block).  The prompt
+# kernels of that file compile to the same code either way.
+EXTRA_FLAGS = {"ls_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

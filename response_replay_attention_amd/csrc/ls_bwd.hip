@@ -386,161 +386,168 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dq(const AttnArgs a) {
   }
 }
 
-// dK or dV of 32 response keys [j0, j0+32) of KV head kv from the query head
-// kv*g + hh, by one wave, key-stationary: loops over the query rows i of that
-// head that see the keys (qoff + i >= j0, in blocks of 32 from
-// i = max(0, j0 - qoff)), accumulating
+// dK or dV of 4 x 32 response keys of KV head kv from the query head
+// kv*g + hh, key-stationary: wave w owns keys [j0, j0+32), j0 = 32*(kb0+w),
+// and the workgroup loops over the query rows of that head that see any of
+// its keys (qoff + i >= 32*kb0, in blocks of 32), accumulating
 //   DV:  dV^T[d][key] += sum_query dO[query][d] P[query][key]
 //   DK:  dK^T[d][key] += sum_query Q[query][d]  dS[query][key]
 // with S = Q K^T and dP = dO V^T recomputed in the (query x key) orientation.
-// The key block's K (and V) rows stay in registers as the B operands of S (and
-// dP).  The Q and dO tiles of query block t+1 are copied into the second of two
-// LDS buffers while block t is computed, and every LDS operand is read four
-// MFMAs ahead of its use (fenced, as in the prompt kernels); one wait per block
-// (ring_barrier) hands the buffers over.  Each head writes its own fp32 partial
-// (k_kv_reduce sums the g heads of a group in head order), so no atomics are
-// needed.
+// The four waves share the Q and dO tiles of each query block, which they copy
+// a quarter each into the second of two LDS buffers while the current block is
+// computed; each wave's K (and V) rows stay in registers as the B operands of
+// S (and dP), loaded once from HBM.  Every LDS operand is read four MFMAs ahead
+// of its use (fenced, as in the prompt kernels); one barrier per block hands
+// the buffers over.  A wave skips the MFMAs of query blocks that see none of
+// its keys.  Each head writes its own fp32 partial (k_kv_reduce sums the g
+// heads of a group in head order), so no atomics are needed.
 template <int D, bool DK>
-__device__ __forceinline__ void resp_kv_wave(const AttnArgs& a, int kv, int hh, int j0,
-                                             uint16_t* smem, float (&s_lse2)[2][kBN],
-                                             float (&s_dval)[2][kBN], int lane) {
+__device__ __forceinline__ void resp_kv_block(const AttnArgs& a, int kv, int hh, int kb0,
+                                              uint16_t* smem, float (&s_lse2)[2][kBN],
+                                              float (&s_dval)[2][kBN], int wave, int lane) {
   constexpr int NKK = D / 16;
   constexpr int NMT = D / 32;
   constexpr int TILE = kBN * D;
-  constexpr int PF = 4;             // LDS prefetch distance, in MFMAs
+  constexpr int PF = 4;                   // LDS prefetch distance, in MFMAs
   constexpr int NA = DK ? 2 * NKK : NKK;  // S (and dP) MFMAs per block, two chains
-  constexpr int NC = 2 * NMT;       // accumulation MFMAs per block
+  constexpr int NC = 2 * NMT;             // accumulation MFMAs per block
   const int hf = lane >> 5, lq = lane & 31;
   const int g = a.hq / a.hkv;
+  const int h = kv * g + hh;
   // Four tiles: Q of buffer b at smem + b TILE, dO of buffer b at
   // smem + (2 + b) TILE (offsets from the one LDS array, so every access stays
-  // an LDS access).  K_r and V_r pass through buffer 1's tiles on their way to
-  // registers, before block 1 is copied there.
-  const BlockLoader<D, 1> ldr(0, lane);
+  // an LDS access).
+  const BlockLoader<D, 4> ldr(wave, lane);
   const Lanes32<D> tl(hf, lq);
 
-  const int nkeys = min(kBN, a.RK - j0);
-  {
-    const size_t off = ((size_t)kv * a.kvr + j0) * D;
-    load_block(ldr, smem + TILE, a.k + off, nkeys);
-    if (DK) load_block(ldr, smem + 3 * TILE, a.v + off, nkeys);
-  }
-  const int h = kv * g + hh;
-  const int ib = max(0, j0 - a.qoff);                  // first query row of the loop
+  const int j0 = (kb0 + wave) * kBN;      // this wave's first key
+  const bool has_keys = j0 < a.RK;
+  const int key = j0 + lq;                // this lane's key column
+  const int ib = max(0, kb0 * kBN - a.qoff);  // first query row of the loop
   const int nblk = ib < a.R ? (a.R - ib + kBN - 1) / kBN : 0;
-  // Q, dO tiles of block t into buffer t & 1; this lane's LSE*log2(e) and D
-  // (query ib + 32t + lane, lanes < 32) into registers, stored after the wait
+
+  // K (and V) rows of this wave's keys as B operands: row key, 16-byte chunk
+  // 2*kk + hf (keys past the response re-read its last row; they are masked)
+  bf16x8 kr[NKK], vr[DK ? NKK : 1];
+  {
+    const size_t r = (size_t)kv * a.kvr + min(key, a.RK - 1);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      kr[kk] = ld_bf16x8(a.k + r * D + 16 * kk + 8 * hf);
+      if (DK) vr[kk] = ld_bf16x8(a.v + r * D + 16 * kk + 8 * hf);
+    }
+  }
+  // Q, dO tiles of block t into buffer t & 1 (a quarter per wave); wave 0's
+  // lanes < 32 load LSE*log2(e) and D of query ib + 32t + lane
   auto issue = [&](int t, float& l2, float& dv) {
     const int i0 = ib + t * kBN, nq = min(kBN, a.R - i0);
-    const bool ok = lane < nq;
-    const size_t r = (size_t)h * a.R + i0 + (ok ? lane : 0);
-    l2 = ok ? a.lse[r] * kLog2e : kInf;
-    dv = ok ? a.dvals[r] : 0.f;
+    if (wave == 0) {
+      const bool ok = lane < nq;
+      const size_t r = (size_t)h * a.R + i0 + (ok ? lane : 0);
+      l2 = ok ? a.lse[r] * kLog2e : kInf;
+      dv = ok ? a.dvals[r] : 0.f;
+    }
     const size_t qo = ((size_t)h * a.R + i0) * D;
     load_block(ldr, smem + (t & 1) * TILE, a.q + qo, nq);
     load_block(ldr, smem + (2 + (t & 1)) * TILE, a.d_o + qo, nq);
   };
 
-  float l2n = kInf, dvn = 0.f;
-  if (nblk > 0) issue(0, l2n, dvn);
-  ring_barrier<0>();  // K_r (V_r) and block 0 have landed
-  bf16x8 kr[NKK], vr[DK ? NKK : 1];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    kr[kk] = tl.row8(smem + TILE, kk);
-    if (DK) vr[kk] = tl.row8(smem + 3 * TILE, kk);
-  }
-  if (lane < kBN) {
-    s_lse2[0][lane] = l2n;
-    s_dval[0][lane] = dvn;
-  }
-  ring_barrier<0>();  // the K_r / V_r reads have returned: buffer 1 is free
-
-  const int key = j0 + lq;  // this lane's key column
   f32x16 acc[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
+  float l2n = kInf, dvn = 0.f;
+  if (nblk > 0) issue(0, l2n, dvn);
+  if (wave == 0 && lane < kBN) {
+    s_lse2[0][lane] = l2n;
+    s_dval[0][lane] = dvn;
+  }
+  ring_barrier<0>();  // block 0 and its LSE, D are in LDS
+
   for (int t = 0; t < nblk; ++t) {
     const int cb = t & 1;
     if (t + 1 < nblk) issue(t + 1, l2n, dvn);
     const int i0 = ib + t * kBN, nq = min(kBN, a.R - i0);
-    const uint16_t* q = smem + cb * TILE;
-    const uint16_t* d_o = smem + (2 + cb) * TILE;
-    // this lane's 16 queries crow(r, hf) = 8*(r/4) + 4*hf + r%4: four runs of 4
-    f32x4 lse4[4], dv4[4];
+    // the block's last query sees this wave's first key
+    if (has_keys && a.qoff + i0 + nq - 1 >= j0) {
+      const uint16_t* q = smem + cb * TILE;
+      const uint16_t* d_o = smem + (2 + cb) * TILE;
+      // this lane's 16 queries crow(r, hf) = 8*(r/4) + 4*hf + r%4: four runs of 4
+      f32x4 lse4[4], dv4[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      lse4[r4] = *reinterpret_cast<const f32x4*>(&s_lse2[cb][8 * r4 + 4 * hf]);
-      if (DK) dv4[r4] = *reinterpret_cast<const f32x4*>(&s_dval[cb][8 * r4 + 4 * hf]);
-    }
-
-    // S[query][key] = sum_d Q[query][d] K[key][d] (DV: two chains over even and
-    // odd k-steps; DK: one chain, interleaved with dP = dO V^T)
-    auto aop = [&](int i) -> bf16x8 {
-      if (DK) return (i & 1) ? tl.row8(d_o, i >> 1) : tl.row8(q, i >> 1);
-      return tl.row8(q, i >> 1 | (i & 1) * (NKK / 2));
-    };
-    bf16x8 rf[NA];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) rf[i] = aop(i);
-    f32x16 s0, s1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = 0.f;
-      s1[r] = 0.f;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      if (DK) {
-        if (i & 1) s1 = mfma32(rf[i], vr[i >> 1], s1);
-        else s0 = mfma32(rf[i], kr[i >> 1], s0);
-      } else {
-        const int kk = i >> 1 | (i & 1) * (NKK / 2);
-        if (i & 1) s1 = mfma32(rf[i], kr[kk], s1);
-        else s0 = mfma32(rf[i], kr[kk], s0);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        lse4[r4] = *reinterpret_cast<const f32x4*>(&s_lse2[cb][8 * r4 + 4 * hf]);
+        if (DK) dv4[r4] = *reinterpret_cast<const f32x4*>(&s_dval[cb][8 * r4 + 4 * hf]);
       }
-      if (i + PF < NA) rf[i + PF] = aop(i + PF);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // X^T operand of the accumulation (dO^T for dV, Q^T for dK), first reads
-    const uint16_t* xt = DK ? q : d_o;
-    bf16x8 cf[NC];
-#pragma unroll
-    for (int j = 0; j < PF; ++j) cf[j] = tl.col8(xt, j / NMT, j % NMT);
 
-    // P (or dS) as the B operand: register 8*ks + e holds query kperm(ks,hf,e)
-    bf16x8 pb[2];
+      // S[query][key] = sum_d Q[query][d] K[key][d] (DV: two chains over even
+      // and odd k-steps; DK: one chain, interleaved with dP = dO V^T)
+      auto aop = [&](int i) -> bf16x8 {
+        if (DK) return (i & 1) ? tl.row8(d_o, i >> 1) : tl.row8(q, i >> 1);
+        return tl.row8(q, i >> 1 | (i & 1) * (NKK / 2));
+      };
+      bf16x8 rf[NA];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // masked scores enter the exponential as -inf (P = 0): no branch
-      const int qr = crow(r, hf);
-      const bool ok = (qr < nq) & (key < a.RK) & (key <= a.qoff + i0 + qr);
-      const float sc = ok ? (DK ? s0[r] : s0[r] + s1[r]) : -kInf;
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc, a.s2, -lse4[r >> 2][r & 3]));
-      pb[r >> 3][r & 7] = to_bf16(DK ? p * (s1[r] - dv4[r >> 2][r & 3]) : p);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // dV^T (or dK^T)[d][key] += sum_query X^T[d][query] pb[query][key]
+      for (int i = 0; i < PF; ++i) rf[i] = aop(i);
+      f32x16 s0, s1;
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      acc[j % NMT] = mfma32(cf[j], pb[j / NMT], acc[j % NMT]);
-      if (j + PF < NC) cf[j + PF] = tl.col8(xt, (j + PF) / NMT, (j + PF) % NMT);
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = 0.f;
+        s1[r] = 0.f;
+      }
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        if (DK) {
+          if (i & 1) s1 = mfma32(rf[i], vr[i >> 1], s1);
+          else s0 = mfma32(rf[i], kr[i >> 1], s0);
+        } else {
+          const int kk = i >> 1 | (i & 1) * (NKK / 2);
+          if (i & 1) s1 = mfma32(rf[i], kr[kk], s1);
+          else s0 = mfma32(rf[i], kr[kk], s0);
+        }
+        if (i + PF < NA) rf[i + PF] = aop(i + PF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // X^T operand of the accumulation (dO^T for dV, Q^T for dK), first reads
+      const uint16_t* xt = DK ? q : d_o;
+      bf16x8 cf[NC];
+#pragma unroll
+      for (int j = 0; j < PF; ++j) cf[j] = tl.col8(xt, j / NMT, j % NMT);
+
+      // P (or dS) as the B operand: register 8*ks + e holds query kperm(ks,hf,e)
+      bf16x8 pb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // masked scores enter the exponential as -inf (P = 0): no branch
+        const int qr = crow(r, hf);
+        const bool ok = (qr < nq) & (key < a.RK) & (key <= a.qoff + i0 + qr);
+        const float sc = ok ? (DK ? s0[r] : s0[r] + s1[r]) : -kInf;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc, a.s2, -lse4[r >> 2][r & 3]));
+        pb[r >> 3][r & 7] = to_bf16(DK ? p * (s1[r] - dv4[r >> 2][r & 3]) : p);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // dV^T (or dK^T)[d][key] += sum_query X^T[d][query] pb[query][key]
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        acc[j % NMT] = mfma32(cf[j], pb[j / NMT], acc[j % NMT]);
+        if (j + PF < NC) cf[j + PF] = tl.col8(xt, (j + PF) / NMT, (j + PF) % NMT);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // block t+1 has landed and every read of buffer cb has returned
-    ring_barrier<0>();
-    if (t + 1 < nblk && lane < kBN) {
+    // the next block's LSE and D, then: block t+1 has landed and every read of
+    // buffer cb has returned
+    if (t + 1 < nblk && wave == 0 && lane < kBN) {
       s_lse2[cb ^ 1][lane] = l2n;
       s_dval[cb ^ 1][lane] = dvn;
     }
+    ring_barrier<0>();
   }
 
-  if (key < a.RK) {
+  if (has_keys && key < a.RK) {
     const float mul = DK ? a.scale : 1.f;
     float* op = a.kv_part + ((((size_t)(DK ? g : 0) + hh) * a.hkv + kv) * a.RK + key) * D + 4 * hf;
 #pragma unroll
@@ -558,27 +565,28 @@ __device__ __forceinline__ void resp_kv_wave(const AttnArgs& a, int kv, int hh, 
   }
 }
 
-// Response dV and dK in one launch, one work item per (KV head, query head of
-// the group, kind, key block), key block fastest: the dV and dK partials run
-// side by side instead of one launch after the other.  Work items are dealt to
-// the XCDs in contiguous ranges, so the items of a query head -- which all copy
-// that head's Q and dO tiles -- share one XCD's L2.  64 KiB of LDS per
-// workgroup: two workgroups per CU.
+// Response dV and dK in one launch, one workgroup (four waves) per (KV head,
+// query head of the group, kind, four key blocks), key blocks fastest: the dV
+// and dK partials run side by side.  Work items are dealt to the XCDs in
+// contiguous ranges, so the items of a query head -- which all copy that
+// head's Q and dO tiles -- share one XCD's L2.  64 KiB of LDS per workgroup.
 template <int D>
-__global__ void __launch_bounds__(64, 1) k_bwd_resp_kv(const AttnArgs a) {
+__global__ void __launch_bounds__(256, 1) k_bwd_resp_kv(const AttnArgs a) {
   constexpr int TILE = kBN * D;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // Q x2, dO x2
   __shared__ __attribute__((aligned(16))) float s_lse2[2][kBN], s_dval[2][kBN];
   const int g = a.hq / a.hkv;
-  const int nkb = (a.RK + kBN - 1) / kBN;
+  const int nkb4 = ((a.RK + kBN - 1) / kBN + 3) / 4;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int kb = w % nkb;
-  const int rest = w / nkb;
+  const int kb4 = w % nkb4;
+  const int rest = w / nkb4;
   const int dk = rest & 1;
   const int hh = (rest >> 1) % g;
   const int kv = (rest >> 1) / g;
-  if (!dk) resp_kv_wave<D, false>(a, kv, hh, kb * kBN, smem, s_lse2, s_dval, threadIdx.x);
-  else resp_kv_wave<D, true>(a, kv, hh, kb * kBN, smem, s_lse2, s_dval, threadIdx.x);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (!dk) resp_kv_block<D, false>(a, kv, hh, 4 * kb4, smem, s_lse2, s_dval, wave, lane);
+  else resp_kv_block<D, true>(a, kv, hh, 4 * kb4, smem, s_lse2, s_dval, wave, lane);
 }
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s) {
@@ -595,7 +603,8 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, h
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t s) {
-  dim3 g(((a.RK + kBN - 1) / kBN) * a.hkv * 2 * (a.hq / a.hkv)), b(64);
+  const int nkb4 = ((a.RK + kBN - 1) / kBN + 3) / 4;
+  dim3 g(nkb4 * a.hkv * 2 * (a.hq / a.hkv)), b(256);
   if (head_dim == 256) hipLaunchKernelGGL((k_bwd_resp_kv<256>), g, b, 0, s, a);
   else hipLaunchKernelGGL((k_bwd_resp_kv<128>), g, b, 0, s, a);
   return hipGetLastError();
