@@ -61,44 +61,57 @@ __device__ __forceinline__ void block_dq(f32x16 (&acc)[D / 32], const Lanes32<D>
   }
 }
 
-// One block of a score wave: S^T = K Q^T and dP^T = V dO^T (the two products
-// interleaved, each operand read PF MFMAs ahead), then dS^T = P^T (dP^T - D),
-// stored to dsw as the two bf16 B operands of the dQ product, in this lane's
-// register order ([ks][lane][8] elements), for the dQ wave of the same rows.
+// One block of a score wave: S^T = K Q^T (two chains, over even and odd
+// k-steps), then dP^T = V dO^T with the exponential of one score placed
+// between consecutive dP MFMAs (P = exp2(S s log2e - LSE log2e)), so that
+// after the last MFMA only dS^T = P^T (dP^T - D) remains; dS^T is stored to dsw
+// as the two bf16 B operands of the dQ product, in this lane's register order
+// ([ks][lane][8] elements), for the dQ wave of the same rows.  Each operand is
+// read PF MFMAs ahead.
 template <int D>
 __device__ __forceinline__ void score_block(const Lanes32<D>& tl, const uint16_t* kt,
                                             const uint16_t* vt, const bf16x8 (&qr)[D / 16],
                                             const bf16x8 (&dor)[D / 16], float s2, float lse2,
                                             float dval, uint16_t* dsw) {
-  constexpr int NS = D / 16;
-  constexpr int NA = 2 * NS;  // score + dP MFMAs per block
+  constexpr int NS = D / 16;  // S MFMAs = dP MFMAs per block
   constexpr int PF = 4;       // LDS prefetch distance, in MFMAs
-  bf16x8 rf[NA];
+  static_assert(16 % NS == 0, "scores spread evenly over the dP MFMAs");
+  bf16x8 kf[NS], vf[NS];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) rf[i] = (i & 1) ? tl.row8(vt, i >> 1) : tl.row8(kt, i >> 1);
-  f32x16 s, dp;
+  for (int i = 0; i < PF; ++i) kf[i] = tl.row8(kt, i);
+  f32x16 sa, sb, dp;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s[r] = 0.f;
+    sa[r] = 0.f;
+    sb[r] = 0.f;
     dp[r] = -dval;  // the accumulation starts at -D: it ends at dP - D
   }
   __builtin_amdgcn_sched_barrier(0);
+  // S = K Q^T over even (sa) and odd (sb) k-steps; the last reads fetch V
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    if (i & 1) dp = mfma32(rf[i], dor[i >> 1], dp);
-    else s = mfma32(rf[i], qr[i >> 1], s);
-    if (i + PF < NA) {
-      const int n = i + PF;
-      rf[n] = (n & 1) ? tl.row8(vt, n >> 1) : tl.row8(kt, n >> 1);
+  for (int i = 0; i < NS; ++i) {
+    if (i & 1) sb = mfma32(kf[i], qr[i], sb);
+    else sa = mfma32(kf[i], qr[i], sa);
+    if (i + PF < NS) kf[i + PF] = tl.row8(kt, i + PF);
+    else vf[i + PF - NS] = tl.row8(vt, i + PF - NS);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // dP^T = V dO^T, with P = exp2(S s log2e - LSE log2e) of one score per MFMA
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    dp = mfma32(vf[i], dor[i], dp);
+    if (i + PF < NS) vf[i + PF] = tl.row8(vt, i + PF);
+#pragma unroll
+    for (int r = i * (16 / NS); r < (i + 1) * (16 / NS); ++r) {
+      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r] + sb[r], s2, -lse2));
+      asm volatile("" : "+v"(p[r]));  // computed here, between the MFMAs
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   bf16x8 dsb[2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], s2, -lse2));
-    dsb[r >> 3][r & 7] = to_bf16(p * dp[r]);
-  }
+  for (int r = 0; r < 16; ++r) dsb[r >> 3][r & 7] = to_bf16(p[r] * dp[r]);
   *reinterpret_cast<bf16x8*>(dsw) = dsb[0];
   *reinterpret_cast<bf16x8*>(dsw + 64 * 8) = dsb[1];
 }
