@@ -169,54 +169,6 @@ struct LanesCM {
   }
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Asynchronous copies of [32][D] bf16 blocks (row stride D) into LDS tiles,
-// spread over the NW waves of the workgroup with global_load_lds_dwordx4 (lane
-// i of a wave instruction lands at LDS base + 16*i; the probe of this
-// instruction confirmed the mapping).  Each lane's source offset inside a block
-// is fixed, so it is computed once.  Rows >= nvalid (1 <= nvalid < 32) re-read
-// row nvalid-1, so a tile always holds finite data; callers mask those rows.
-// Completion: s_waitcnt vmcnt + barrier.
-template <int D, int NW = 4>
-struct TileLoader {
-  static constexpr int NIW = (kBN * D * 2 / 1024) / NW;  // wave instructions per block
-  static_assert(NIW * NW * 1024 == kBN * D * 2, "tile must split evenly over the waves");
-  int off[NIW];  // element offset of this lane's 16 bytes in the source block
-  int row[NIW];
-  int blk0;
-  __device__ __forceinline__ TileLoader(int wave, int lane) : blk0(wave * NIW) {
-#pragma unroll
-    for (int j = 0; j < NIW; ++j) {
-      const int e = (blk0 + j) * 512 + 8 * lane;  // element position this lane fills
-      row[j] = e / D;
-      off[j] = row[j] * D + ((((e % D) >> 3) ^ swf(row[j])) << 3);
-    }
-  }
-  __device__ __forceinline__ void load(uint16_t* tile, const uint16_t* g, int nvalid) const {
-    if (nvalid >= kBN) {
-#pragma unroll
-      for (int j = 0; j < NIW; ++j)
-        __builtin_amdgcn_global_load_lds(g + off[j], (lds_ptr_t)(tile + (blk0 + j) * 512), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NIW; ++j) {
-        const int shift = row[j] < nvalid ? 0 : (nvalid - 1 - row[j]) * D;
-        __builtin_amdgcn_global_load_lds(g + off[j] + shift, (lds_ptr_t)(tile + (blk0 + j) * 512),
-                                         16, 0, 0);
-      }
-    }
-  }
-};
-
-// One-shot form of TileLoader::load (for kernels that load few tiles).
-template <int D, int NW = 4>
-__device__ __forceinline__ void tile_load_async(uint16_t* tile, const uint16_t* g, int nvalid,
-                                                int wave, int lane) {
-  const TileLoader<D, NW> tl(wave, lane);
-  tl.load(tile, g, nvalid);
-}
-
 // Block copies through the buffer path: buffer_load_dwordx4 ... lds with a
 // raw descriptor whose base is the block's first row (uniform, in SGPRs) and a
 // per-lane byte offset that never changes, so a copy costs no per-lane address
@@ -420,15 +372,6 @@ struct KeyWalk {
     }
     return 0;
   }
-  // start the asynchronous copy of block b's K and V into tiles kt, vt
-  __device__ __forceinline__ void issue(int b, uint16_t* kt, uint16_t* vt, int wave, int lane,
-                                        int& nvalid, int& key0) const {
-    const size_t off = block(b, nvalid, key0);
-    if (nvalid > 0) {
-      tile_load_async<D>(kt, a.k + off, nvalid, wave, lane);
-      tile_load_async<D>(vt, a.v + off, nvalid, wave, lane);
-    }
-  }
 };
 
 // Wait until at most N of this wave's vector-memory loads (including the
@@ -461,70 +404,6 @@ template <int N>
 __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<N, true>());
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// acc *= alpha for an accumulator tile that lives in AGPRs.  Plain C++ would
-// make the compiler give the loop-carried accumulators VGPR class (VALU cannot
-// read AGPRs) and copy every one of them AGPR<->VGPR on every iteration; the
-// in-place read/multiply/write keeps them in AGPRs.  Only used on the rare
-// rescale path, long after the MFMAs that wrote these registers.
-__device__ __forceinline__ void scale_acc(f32x4& acc, float alpha) {
-  float x0 = acc[0], x1 = acc[1], x2 = acc[2], x3 = acc[3], t;
-  asm volatile(
-      "v_accvgpr_read_b32 %4, %0\n\t"
-      "v_mul_f32 %4, %5, %4\n\t"
-      "v_accvgpr_write_b32 %0, %4\n\t"
-      "v_accvgpr_read_b32 %4, %1\n\t"
-      "v_mul_f32 %4, %5, %4\n\t"
-      "v_accvgpr_write_b32 %1, %4\n\t"
-      "v_accvgpr_read_b32 %4, %2\n\t"
-      "v_mul_f32 %4, %5, %4\n\t"
-      "v_accvgpr_write_b32 %2, %4\n\t"
-      "v_accvgpr_read_b32 %4, %3\n\t"
-      "v_mul_f32 %4, %5, %4\n\t"
-      "v_accvgpr_write_b32 %3, %4"
-      : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(t)
-      : "v"(alpha));
-  acc = f32x4{x0, x1, x2, x3};
-}
-// Zero an accumulator tile directly in AGPRs (see scale_acc).
-__device__ __forceinline__ void zero_acc(f32x4& acc) {
-  float x0, x1, x2, x3;
-  asm volatile(
-      "v_accvgpr_write_b32 %0, 0\n\t"
-      "v_accvgpr_write_b32 %1, 0\n\t"
-      "v_accvgpr_write_b32 %2, 0\n\t"
-      "v_accvgpr_write_b32 %3, 0"
-      : "=a"(x0), "=a"(x1), "=a"(x2), "=a"(x3));
-  acc = f32x4{x0, x1, x2, x3};
-}
-// Copy an AGPR accumulator tile to ordinary registers (see scale_acc).
-__device__ __forceinline__ f32x4 read_acc(const f32x4& acc) {
-  float x0 = acc[0], x1 = acc[1], x2 = acc[2], x3 = acc[3], y0, y1, y2, y3;
-  asm volatile(
-      "v_accvgpr_read_b32 %0, %4\n\t"
-      "v_accvgpr_read_b32 %1, %5\n\t"
-      "v_accvgpr_read_b32 %2, %6\n\t"
-      "v_accvgpr_read_b32 %3, %7"
-      : "=v"(y0), "=v"(y1), "=v"(y2), "=v"(y3)
-      : "a"(x0), "a"(x1), "a"(x2), "a"(x3));
-  return f32x4{y0, y1, y2, y3};
-}
-__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f32x4 part = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-    scale_acc(part, alpha);
-    acc[4 * q] = part[0];
-    acc[4 * q + 1] = part[1];
-    acc[4 * q + 2] = part[2];
-    acc[4 * q + 3] = part[3];
-  }
-}
-
-__device__ __forceinline__ f32x4 read_acc4(const f32x16& acc, int q) {
-  const f32x4 part = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-  return read_acc(part);
 }
 
 // fp32 -> bf16 with round-to-nearest-even.
