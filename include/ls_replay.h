@@ -29,8 +29,11 @@
  *     the layouts stated below.  bf16 = IEEE bfloat16 (1-8-7).
  *   - GPU work is enqueued asynchronously on `stream` (0 = null stream).  A
  *     device fault surfaces at the caller's next synchronisation.
- *   - All argument checks happen before any HIP call, so a call that returns
- *     an error has enqueued nothing.
+ *   - All argument checks happen before any HIP call: a call that returns
+ *     LS_ERR_INVALID_ARG, LS_ERR_UNSUPPORTED, LS_ERR_PAGE_RANGE or
+ *     LS_ERR_WORKSPACE has enqueued nothing.  LS_ERR_HIP reports a failed
+ *     launch or runtime call and may follow launches the same call already
+ *     enqueued; the outputs are then undefined.
  *   - Supported: head_dim in {128, 256}; page_size == 256; Hq % Hkv == 0;
  *     resp_len >= 1; prompt_len >= 0; Hq*resp_len*head_dim < 2^31;
  *     Hkv*kv_rows*head_dim < 2^31.
@@ -111,9 +114,11 @@ typedef struct ls_attn_shape {
  *   split_offsets       device int32 [num_splits + 1]: CSR offsets into order.
  *   split_offsets_host  host copy of split_offsets (used to size the launch).
  * Logical page p holds prompt positions [p*page_size, (p+1)*page_size); only
- * the last page may be partial (positions >= prompt_len are masked).  A page
- * id outside its range seen by a kernel is skipped (treated as empty), so a
- * corrupted device table gives wrong numbers, never an out-of-bounds read. */
+ * the last page may be partial (positions >= prompt_len are masked).  The
+ * kernels trust the device copies to match what ls_kv_page_table validated;
+ * a corrupted device table gives wrong values but never an out-of-bounds
+ * access (a page whose id is out of range is read as pool block 0 by the
+ * unmasked key loop and skipped by the masked one). */
 typedef struct ls_page_table {
   const int32_t* l2p;
   const int32_t* order;
@@ -171,9 +176,12 @@ size_t ls_replay_attn_bwd_workspace(const ls_attn_shape* shape, const ls_page_ta
  *                 included).
  *   x_j = scale * <q[h,i], k_j>;  part_m[c,row] = m, part_l[c,row] = sum_j exp(x_j - m),
  *   part_o[c,row,:] = sum_j exp(x_j - m) v_j / part_l[c,row].
- * m is a shift chosen by the kernel (within a few units of max_j x_j, never
- * below it by more than 8*ln2); the pair (m, l) is what is defined: m + ln l is
- * the split's log-sum-exp.  An empty split gives m = -inf, l = 0, o = 0.
+ * m is a shift chosen by the kernel, the largest score of the split's first
+ * key block, or the split's maximum when a later score exceeds that by more
+ * than 32*ln2: so max_j x_j - 32*ln2 <= m <= max_j x_j (32*ln2 ~ 22.2), up to
+ * fp32 rounding, and l <= 2^32 * (number of keys).  The pair (m, l) is what
+ * is defined: m + ln l is the split's log-sum-exp.  An empty split gives
+ * m = -inf, l = 0, o = 0.
  *   q                 device bf16 [Hq, R, d]
  *   k_pool, v_pool    device bf16 [num_phys_pages, Hkv, page_size, d]
  *   k_resp, v_resp    device bf16 [Hkv, kv_rows, d] (rows < q_offset + R are read)
@@ -292,8 +300,9 @@ ls_status ls_replay_attn_bwd(const ls_attn_shape* shape, const ls_page_table* pt
  * launches is bracketed by a pair of hipEvents recorded on the launch stream.
  * ls_timing_read synchronises those events and returns, for the named kernel,
  * the number of launches and their summed duration since the last reset.
- * Kernel names: "fwd_prompt", "fwd_resp", "fwd_combine", "lse_merge",
- * "bwd_dot", "bwd_prompt_dq", "bwd_resp_dq", "bwd_resp_dkdv", "dq_reduce".
+ * Kernel names: "resolve_pages", "fwd_prompt", "fwd_combine", "fwd_resp",
+ * "lse_merge", "bwd_dot", "bwd_prompt_dq", "bwd_resp_dq", "bwd_resp_dkdv",
+ * "kv_reduce", "dq_reduce", "page_append".
  * ls_timing_enable(0) stops recording; ls_timing_reset drops all records.
  * Not thread-safe; calls overlapping on several host threads race. */
 ls_status ls_timing_enable(int32_t on);

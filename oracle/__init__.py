@@ -25,5 +25,6 @@ from .attention import (  # noqa: F401
     replay_backward,
     partial_stats,
     lse_merge,
+    response_kv_grads,
 )
 from .page_table import split_pages  # noqa: F401

@@ -203,3 +203,51 @@ def lse_merge(mx, l_, o):
     out = np.einsum("sn,snd->nd", w, o) / safe[:, None]
     lse = np.where(tot > 0, big + np.log(safe), -np.inf)
     return out, lse
+
+
+def _resp_visible(tok: np.ndarray, rk: int) -> np.ndarray:
+    """``[n, rk]`` visibility of response keys ``0..rk-1`` to response tokens
+    ``tok`` (causal, diagonal included)."""
+    return np.arange(rk)[None, :] <= tok[:, None]
+
+
+def response_kv_grads(q, k_resp, v_resp, d_o, lse, dvals, scale: float, q_offset: int = 0):
+    """dK_r and dV_r of the response keys from given softmax statistics.
+
+    The prompt enters the response-key gradients only through each row's LSE
+    (the softmax normaliser) and D = <dO, O>; given those two, the gradient of
+    the response keys is a sum over response rows and response keys alone
+    (the backward of the pages' response-only objective with the prompt state
+    detached; LongStraw abstract, cortexa.online; DeepRead summary, "Method").
+
+    q, d_o ``[Hq, R, d]`` are rows ``q_offset .. q_offset+R-1`` of the
+    response; k_resp, v_resp ``[Hkv, >= q_offset+R, d]`` (the first
+    ``q_offset + R`` rows are the keys); lse, dvals ``[Hq, R]`` (natural-log
+    LSE and D).  For query head h, kv = h // g, row i (token t = q_offset + i)
+    and response key j <= t:
+        p_ij  = exp(s <Q[h,i], Kr[kv,j]> - LSE[h,i])
+        dS_ij = p_ij (<dO[h,i], Vr[kv,j]> - D[h,i])
+        dVr[kv,j] = sum_h sum_i p_ij dO[h,i]
+        dKr[kv,j] = s sum_h sum_i dS_ij Q[h,i]
+    Returns ``dK_r, dV_r [Hkv, q_offset + R, d]`` (float64): the contribution
+    of these rows (all of it for a whole response).
+    """
+    q, kr, vr, do = (as_f64(t) for t in (q, k_resp, v_resp, d_o))
+    lse, dvals = as_f64(lse), as_f64(dvals)
+    hq, r, d = q.shape
+    hkv = kr.shape[0]
+    g = hq // hkv
+    rk = q_offset + r
+    kr, vr = kr[:, :rk], vr[:, :rk]
+    vis = _resp_visible(q_offset + np.arange(r), rk)          # [R, rk]
+    dk = np.zeros((hkv, rk, d))
+    dv = np.zeros((hkv, rk, d))
+    for h in range(hq):
+        kv = h // g
+        x = scale * (q[h] @ kr[kv].T)                           # [R, rk]
+        p = np.where(vis, np.exp(np.where(vis, x, 0.0) - lse[h][:, None]), 0.0)
+        dp = do[h] @ vr[kv].T                                   # <dO_i, V_j>
+        ds = p * (dp - dvals[h][:, None])
+        dv[kv] += p.T @ do[h]
+        dk[kv] += scale * (ds.T @ q[h])
+    return dk, dv

@@ -100,6 +100,11 @@ def test_split_partials_match_oracle(shape):
             if (~empty).any():
                 assert_lse_close(f"part{c} h{h} lse", gm[~empty] + np.log(gl[~empty]),
                                  m[~empty] + np.log(l_[~empty]))
+                # the documented range of the shift: max - 32 ln 2 <= m <= max
+                tol = 1e-4 * np.maximum(1.0, np.abs(m[~empty]))
+                assert np.all(gm[~empty] <= m[~empty] + tol), f"part{c} h{h}: shift above the max"
+                assert np.all(gm[~empty] >= m[~empty] - 32 * math.log(2) - tol), \
+                    f"part{c} h{h}: shift more than 32 ln 2 below the max"
                 assert_close(f"part{c} h{h} o", to_np(fwd.part_o[c, h])[~empty], o[~empty])
             assert np.all(to_np(fwd.part_o[c, h])[empty] == 0)
 

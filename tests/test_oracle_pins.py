@@ -245,6 +245,77 @@ def test_row_block_contributions_match_masked_autograd():
     np.testing.assert_allclose(dv_sum, dvr_all, atol=1e-12, rtol=0)
 
 
+@pytest.mark.parametrize("hq,hkv,d,p,r", [(6, 1, 16, 40, 9), (6, 2, 32, 70, 16), (4, 2, 8, 0, 6),
+                                         (8, 2, 24, 1, 33)])
+def test_response_kv_grads_from_statistics_equal_autograd(hq, hkv, d, p, r):
+    """dK_r, dV_r from the statistics alone: with LSE from scipy's logsumexp of
+    the full causal score rows and D from torch's SDPA output, they equal
+    autograd's response-key gradients of the full-sequence attention with the
+    prompt detached."""
+    q, kp, vp, kr, vr, do = _problem(hq, hkv, d, p, r, seed=7 * d + p)
+    s = 1 / math.sqrt(d)
+    out, (_, _, _, tkr, tvr) = _full_sequence_sdpa(q, kp, vp, kr, vr, s, grad=True)
+    (out * torch.tensor(do)).sum().backward()
+    lse = _full_sequence_lse(q, kp, kr, s)
+    dvals = (out.detach().numpy() * do).sum(-1)
+    dk, dv = oracle.response_kv_grads(q, kr, vr, do, lse, dvals, s)
+    np.testing.assert_allclose(dk, tkr.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tvr.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_response_kv_grads_of_token_blocks_equal_masked_autograd():
+    """A token block's rows at q_offset, with the statistics of the whole
+    response, give autograd's response-key gradients of <dO, O> with dO zero
+    outside the block; keys after the block get nothing, and the blocks sum to
+    the whole response's gradient."""
+    q, kp, vp, kr, vr, do = _problem(6, 2, 16, 37, 23, seed=41)
+    s = 0.25
+    out, _ = _full_sequence_sdpa(q, kp, vp, kr, vr, s)
+    lse = _full_sequence_lse(q, kp, kr, s)
+    dvals = (out.detach().numpy() * do).sum(-1)
+    dk_all, dv_all = oracle.response_kv_grads(q, kr, vr, do, lse, dvals, s)
+    dk_sum, dv_sum = np.zeros_like(dk_all), np.zeros_like(dv_all)
+    for b0, b1 in ((0, 6), (6, 13), (13, 23)):
+        out, (_, _, _, tkr, tvr) = _full_sequence_sdpa(q, kp, vp, kr, vr, s, grad=True)
+        mask = np.zeros_like(do)
+        mask[:, b0:b1] = 1.0
+        (out * torch.tensor(do * mask)).sum().backward()
+        dk_b, dv_b = oracle.response_kv_grads(q[:, b0:b1], kr, vr, do[:, b0:b1], lse[:, b0:b1],
+                                              dvals[:, b0:b1], s, q_offset=b0)
+        assert dk_b.shape == (2, b1, 16)
+        np.testing.assert_allclose(dk_b, tkr.grad.numpy()[:, :b1], atol=1e-11, rtol=0)
+        np.testing.assert_allclose(dv_b, tvr.grad.numpy()[:, :b1], atol=1e-11, rtol=0)
+        assert not tkr.grad.numpy()[:, b1:].any()
+        dk_sum[:, :b1] += dk_b
+        dv_sum[:, :b1] += dv_b
+    np.testing.assert_allclose(dk_sum, dk_all, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv_sum, dv_all, atol=1e-12, rtol=0)
+
+
+def test_response_kv_grads_planted_mistakes_are_caught(monkeypatch):
+    """The autograd pin above fails when the causal mask of the response keys
+    is wrong (diagonal dropped, or one key too many)."""
+    q, kp, vp, kr, vr, do = _problem(6, 2, 16, 30, 11, seed=43)
+    s = 0.25
+    out, (_, _, _, tkr, tvr) = _full_sequence_sdpa(q, kp, vp, kr, vr, s, grad=True)
+    (out * torch.tensor(do)).sum().backward()
+    lse = _full_sequence_lse(q, kp, kr, s)
+    dvals = (out.detach().numpy() * do).sum(-1)
+
+    def pin_holds():
+        dk, dv = oracle.response_kv_grads(q, kr, vr, do, lse, dvals, s)
+        return (np.abs(dk - tkr.grad.numpy()).max() < 1e-11
+                and np.abs(dv - tvr.grad.numpy()).max() < 1e-11)
+
+    good = oatt._resp_visible
+    assert pin_holds()
+    for bad in (lambda tok, rk: good(tok - 1, rk), lambda tok, rk: good(tok + 1, rk)):
+        monkeypatch.setattr(oatt, "_resp_visible", bad)
+        assert not pin_holds()
+    monkeypatch.setattr(oatt, "_resp_visible", good)
+    assert pin_holds()
+
+
 def _split_parts(q, kp, vp, kr, vr, s, order, offsets):
     """Per-split statistics for every (head,row), the response block last."""
     hq, r, d = q.shape
