@@ -224,6 +224,33 @@ ls_status ls_replay_attn_fwd_members(const ls_attn_shape* shape, const ls_page_t
                                      void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* Bytes of the device scratch ls_replay_attn_fwd_noalloc uses (64 MiB). */
+#define LS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* ls_replay_attn_fwd_noalloc -- ls_replay_attn_fwd without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Neither this call nor anything it calls allocates memory.
+ *   Arguments, layouts, outputs and errors are those of ls_replay_attn_fwd
+ *   without workspace / workspace_bytes.
+ *   The workspace is the library's own static device array of
+ *   LS_NOALLOC_SCRATCH_BYTES; each GPU the library runs on holds one copy
+ *   until the process ends.  The first call on a device looks up its address
+ *   (host side, once per device).
+ *   The launch plan keeps its internal sub-split partials within the scratch:
+ *   where ls_replay_attn_fwd would use more, this call uses fewer sub-splits
+ *   (same result up to fp32 rounding order, possibly slower).
+ *   LS_ERR_WORKSPACE: the prompt's resolved page list (4 bytes per page,
+ *   rounded up to 256) does not fit in the scratch (over ~16.7M pages).
+ *   Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ *   contents: calls that overlap on one GPU (two streams, two host threads)
+ *   race, and the caller must order them.  Nothing in the scratch needs to
+ *   start at zero: a call reads only bytes it wrote earlier in the same call. */
+ls_status ls_replay_attn_fwd_noalloc(const ls_attn_shape* shape, const ls_page_table* pt,
+                                     const void* q, const void* k_pool, const void* v_pool,
+                                     const void* k_resp, const void* v_resp, float* part_o,
+                                     float* part_m, float* part_l, hipStream_t stream);
+
 /* ls_kv_page_append -- the capture-side page writer: stores the K and V of
  * T freshly prefilled prompt tokens as compact pages of the pool (the shared
  * prompt is prefilled once without a graph and only the per-token K/V of the

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     LS_ACCUMULATE_KV,
     LS_SPLIT_BLOCK_CYCLIC,
     LS_SPLIT_CONTIGUOUS,
+    LS_NOALLOC_SCRATCH_BYTES,
     LS_SPLIT_EXPLICIT,
     AttnShape,
     LsError,
@@ -26,6 +27,7 @@ from .binding import (  # noqa: F401
     ls_replay_attn_bwd_workspace,
     ls_replay_attn_fwd,
     ls_replay_attn_fwd_members,
+    ls_replay_attn_fwd_noalloc,
     ls_replay_attn_fwd_workspace,
     ls_status_string,
     ls_timing_enable,

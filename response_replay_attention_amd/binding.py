@@ -23,12 +23,14 @@ LS_SPLIT_BLOCK_CYCLIC = 1
 LS_SPLIT_EXPLICIT = 2
 LS_ACCUMULATE_KV = 1
 PAGE_SIZE = 256
+LS_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/ls_replay.h declares
 EXPORTS = (
     "ls_status_string", "ls_version", "ls_kv_page_table",
     "ls_replay_attn_fwd_workspace", "ls_replay_attn_bwd_workspace",
-    "ls_replay_attn_fwd", "ls_replay_attn_fwd_members", "ls_kv_page_append", "ls_lse_merge",
+    "ls_replay_attn_fwd", "ls_replay_attn_fwd_members", "ls_replay_attn_fwd_noalloc",
+    "ls_kv_page_append", "ls_lse_merge",
     "ls_replay_attn_bwd",
     "ls_timing_enable", "ls_timing_reset", "ls_timing_read",
 )
@@ -88,6 +90,7 @@ def lib() -> ctypes.CDLL:
         "ls_replay_attn_bwd_workspace": (SZ, [P, P]),
         "ls_replay_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "ls_replay_attn_fwd_members": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "ls_replay_attn_fwd_noalloc": (I32, [P, P, P, P, P, P, P, P, P, P, P]),
         "ls_kv_page_append": (I32, [I32, I32, I32, P, P, P, P, P, P, I32, P]),
         "ls_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P, P]),
         "ls_replay_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -211,6 +214,24 @@ def ls_replay_attn_fwd(shape: AttnShape, pt: PageTable, q, k_pool, v_pool, k_res
         _ptr(part_o, f32, "part_o"), _ptr(part_m, f32, "part_m"), _ptr(part_l, f32, "part_l"),
         _ptr(workspace), ws_bytes, _stream(stream))
     _check("ls_replay_attn_fwd", st)
+
+
+def ls_replay_attn_fwd_noalloc(shape: AttnShape, pt: PageTable, q, k_pool, v_pool, k_resp, v_resp,
+                               part_o, part_m, part_l, stream=None) -> None:
+    """The forward with the library's own device scratch as its workspace:
+    no device memory is allocated by this call or by the library."""
+    bf, f32 = torch.bfloat16, torch.float32
+    _check_attn_tensors(shape, pt, q, k_pool, v_pool, k_resp, v_resp)
+    rows = (pt.num_splits + 1) * shape.num_q_heads * shape.resp_len
+    _expect_at_least(part_o, rows * shape.head_dim, "part_o")
+    _expect_at_least(part_m, rows, "part_m")
+    _expect_at_least(part_l, rows, "part_l")
+    st = lib().ls_replay_attn_fwd_noalloc(
+        ctypes.byref(shape), ctypes.byref(pt), _ptr(q, bf, "q"), _ptr(k_pool, bf, "k_pool"),
+        _ptr(v_pool, bf, "v_pool"), _ptr(k_resp, bf, "k_resp"), _ptr(v_resp, bf, "v_resp"),
+        _ptr(part_o, f32, "part_o"), _ptr(part_m, f32, "part_m"), _ptr(part_l, f32, "part_l"),
+        _stream(stream))
+    _check("ls_replay_attn_fwd_noalloc", st)
 
 
 def ls_replay_attn_fwd_members(shape: AttnShape, pt: PageTable, member_offsets, member_offsets_dev,

@@ -1,6 +1,7 @@
 // Host side of the C ABI (include/ls_replay.h): argument validation, launch
 // planning, the page-split builder and kernel timing.  Every check runs
-// before the first HIP call, so an error return means nothing was enqueued.
+// before the first HIP call, so a validation error means nothing was
+// enqueued; LS_ERR_HIP may follow launches the same call already made.
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
@@ -21,6 +22,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// bytes of the forward's chunk partials (o, m, l) for `units` split chunks
+size_t chunk_part_bytes(const ls_attn_shape& sh, size_t units) {
+  const size_t rows = (size_t)sh.num_q_heads * sh.resp_len;
+  return round_up(units * rows * sh.head_dim * 4, 256) + 2 * round_up(units * rows * 4, 256);
+}
+
 // ---------------------------------------------------------------- planning
 // Internal sub-splitting ("chunks") of every split so that the grid fills the
 // chip: items = S * chunks * Hkv * mtiles workgroups, one per CU at a time.
@@ -33,7 +40,10 @@ struct Plan {
   int units = 0;  // S * chunks
 };
 
-Plan plan_prompt(const ls_attn_shape& sh, const ls_page_table& pt, int rows_per_wg) {
+// part_cap: largest number of bytes the chunk partials may take (chunk counts
+// whose partials exceed it are not considered; one chunk needs none).
+Plan plan_prompt(const ls_attn_shape& sh, const ls_page_table& pt, int rows_per_wg,
+                 size_t part_cap = SIZE_MAX) {
   Plan p;
   const int g = sh.num_q_heads / sh.num_kv_heads;
   const int64_t gr = (int64_t)g * sh.resp_len;
@@ -51,6 +61,7 @@ Plan plan_prompt(const ls_attn_shape& sh, const ls_page_table& pt, int rows_per_
       const int cp = (maxp + c - 1) / c;
       const int chunks = (maxp + cp - 1) / cp;  // chunks actually needed at this size
       if (chunks != c) continue;
+      if (chunks > 1 && chunk_part_bytes(sh, (size_t)pt.num_splits * chunks) > part_cap) continue;
       const int64_t items = base * chunks;
       const int64_t cost = ((items + kTargetWGs - 1) / kTargetWGs) * cp;
       if (best < 0 || cost < best) {
@@ -172,14 +183,10 @@ size_t kv_part_bytes(const ls_attn_shape& sh) {
                   256);
 }
 
-size_t fwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt) {
-  const Plan p = plan_prompt(sh, pt, kFwdRows);
+size_t fwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt, size_t part_cap = SIZE_MAX) {
+  const Plan p = plan_prompt(sh, pt, kFwdRows, part_cap);
   size_t n = phys_bytes(pt);
-  if (p.chunks > 1) {
-    const size_t rows = (size_t)sh.num_q_heads * sh.resp_len;
-    const size_t slots = (size_t)p.units;
-    n += round_up(slots * rows * sh.head_dim * 4, 256) + 2 * round_up(slots * rows * 4, 256);
-  }
+  if (p.chunks > 1) n += chunk_part_bytes(sh, (size_t)p.units);
   return n;
 }
 
@@ -191,24 +198,43 @@ size_t bwd_ws_bytes(const ls_attn_shape& sh, const ls_page_table& pt) {
          kv_part_bytes(sh);
 }
 
-ls_status fwd_impl(const ls_attn_shape* sh, const ls_page_table* pt, int32_t nmem,
-                   const int32_t* moffs_dev, const void* q,
+}  // namespace
+
+size_t ls::ws_phys_bytes(const ls_page_table& pt) { return phys_bytes(pt); }
+
+// Host checks of a forward call's shape, table and pointers (no HIP call).
+ls_status ls::fwd_check_args(const ls_attn_shape* sh, const ls_page_table* pt, const void* q,
                              const void* k_pool, const void* v_pool, const void* k_resp,
-                             const void* v_resp, float* part_o, float* part_m, float* part_l,
-                             void* ws, size_t ws_bytes, hipStream_t stream) {
+                             const void* v_resp, const float* part_o, const float* part_m,
+                             const float* part_l) {
   ls_status st = check_shape(sh);
   if (st != LS_OK) return st;
   if ((st = check_table(sh, pt)) != LS_OK) return st;
   if (!q || !k_resp || !v_resp || !part_o || !part_m || !part_l) return LS_ERR_INVALID_ARG;
   if (pt->num_pages > 0 && (!k_pool || !v_pool)) return LS_ERR_INVALID_ARG;
   for (const void* p : {q, k_pool, v_pool, k_resp, v_resp, (const void*)part_o,
-                        (const void*)part_m, (const void*)part_l, (const void*)ws})
+                        (const void*)part_m, (const void*)part_l})
     if (p && !aligned16(p)) return LS_ERR_INVALID_ARG;
-  const size_t need = fwd_ws_bytes(*sh, *pt);
+  return LS_OK;
+}
+
+size_t ls::fwd_ws_need(const ls_attn_shape& sh, const ls_page_table& pt, size_t part_cap) {
+  return fwd_ws_bytes(sh, pt, part_cap);
+}
+
+ls_status ls::fwd_launch(const ls_attn_shape* sh, const ls_page_table* pt, int32_t nmem,
+                         const int32_t* moffs_dev, const void* q, const void* k_pool,
+                         const void* v_pool, const void* k_resp, const void* v_resp,
+                         float* part_o, float* part_m, float* part_l, void* ws, size_t ws_bytes,
+                         size_t part_cap, hipStream_t stream) {
+  ls_status st = fwd_check_args(sh, pt, q, k_pool, v_pool, k_resp, v_resp, part_o, part_m, part_l);
+  if (st != LS_OK) return st;
+  if (ws && !aligned16(ws)) return LS_ERR_INVALID_ARG;
+  const size_t need = fwd_ws_bytes(*sh, *pt, part_cap);
   if (need > 0 && (!ws || ws_bytes < need)) return LS_ERR_WORKSPACE;
   if (need == 0) ws = nullptr;
 
-  const Plan plan = plan_prompt(*sh, *pt, kFwdRows);
+  const Plan plan = plan_prompt(*sh, *pt, kFwdRows, part_cap);
   const size_t rows = (size_t)sh->num_q_heads * sh->resp_len;
   const int d = sh->head_dim;
   AttnArgs a = base_args(*sh, *pt, q, k_pool, v_pool);
@@ -264,6 +290,16 @@ ls_status fwd_impl(const ls_attn_shape* sh, const ls_page_table* pt, int32_t nme
   return run("fwd_resp", stream, [&] { return launch_fwd(r, d, true, rgrid, stream); });
 }
 
+namespace {
+
+ls_status fwd_impl(const ls_attn_shape* sh, const ls_page_table* pt, int32_t nmem,
+                   const int32_t* moffs_dev, const void* q, const void* k_pool,
+                   const void* v_pool, const void* k_resp, const void* v_resp, float* part_o,
+                   float* part_m, float* part_l, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fwd_launch(sh, pt, nmem, moffs_dev, q, k_pool, v_pool, k_resp, v_resp, part_o, part_m,
+                    part_l, ws, ws_bytes, SIZE_MAX, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -280,7 +316,7 @@ const char* ls_status_string(ls_status s) {
   return "unknown status";
 }
 
-int32_t ls_version(void) { return 101; }
+int32_t ls_version(void) { return 102; }
 
 ls_status ls_kv_page_table(int32_t num_pages, int32_t page_size, int64_t prompt_len,
                            const int32_t* l2p, int32_t num_phys_pages, int32_t num_splits,

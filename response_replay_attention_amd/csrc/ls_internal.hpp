@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "ls_replay.h"
+
 namespace ls {
 
 constexpr int kPage = 256;       // prompt tokens per page (only size supported)
@@ -53,6 +55,22 @@ struct AttnArgs {
   float* dv;
   float* kv_part;         // fp32 [2][g][Hkv][RK][d] per-query-head dV (0) / dK (1) partials
 };
+
+// Host checks of a forward call's shape, table and pointers (no HIP call);
+// the workspace bytes a forward needs when the chunk partials of its launch
+// plan may take at most part_cap bytes (SIZE_MAX: the plan that fills the
+// chip); and the checked forward under that cap.
+ls_status fwd_check_args(const ls_attn_shape* sh, const ls_page_table* pt, const void* q,
+                         const void* k_pool, const void* v_pool, const void* k_resp,
+                         const void* v_resp, const float* part_o, const float* part_m,
+                         const float* part_l);
+size_t fwd_ws_need(const ls_attn_shape& sh, const ls_page_table& pt, size_t part_cap);
+ls_status fwd_launch(const ls_attn_shape* sh, const ls_page_table* pt, int32_t nmem,
+                     const int32_t* moffs_dev, const void* q, const void* k_pool, const void* v_pool,
+                     const void* k_resp, const void* v_resp, float* part_o, float* part_m,
+                     float* part_l, void* ws, size_t ws_bytes, size_t part_cap, hipStream_t stream);
+// bytes of the resolved page list at the start of a workspace
+size_t ws_phys_bytes(const ls_page_table& pt);
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s);
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, bool resp, int grid, hipStream_t s);

@@ -226,6 +226,34 @@ def test_workspace_checks():
     assert _fwd(big, bt, ws=0) == WORKSPACE
 
 
+def _fwd_noalloc(sh, pt, **ptrs):
+    p = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, k_resp=FAKE, v_resp=FAKE, part_o=FAKE,
+             part_m=FAKE, part_l=FAKE)
+    p.update(ptrs)
+    return rra.lib().ls_replay_attn_fwd_noalloc(ctypes.byref(sh), ctypes.byref(pt), p["q"],
+                                                p["k_pool"], p["v_pool"], p["k_resp"],
+                                                p["v_resp"], p["part_o"], p["part_m"],
+                                                p["part_l"], None)
+
+
+def test_noalloc_forward_checks_before_any_hip_call():
+    """The allocation-free forward returns the same validation errors as the
+    forward (no GPU here: each return happens before any HIP call), and
+    refuses a prompt whose resolved page list does not fit its scratch."""
+    assert B.LS_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert _fwd_noalloc(_shape(head_dim=64), _table()) == UNSUPPORTED
+    assert _fwd_noalloc(_shape(resp_len=0), _table()) == INVALID
+    assert _fwd_noalloc(_shape(), _table(offs=[0, 3, 2])) == INVALID
+    assert _fwd_noalloc(_shape(), _table(l2p=0)) == INVALID
+    for name in ("q", "k_resp", "v_resp", "part_o", "part_m", "part_l", "k_pool"):
+        assert _fwd_noalloc(_shape(), _table(), **{name: 0}) == INVALID
+        assert _fwd_noalloc(_shape(), _table(), **{name: FAKE + 2}) == INVALID
+    pages = (64 << 20) // 4 + 1      # 4 bytes per page: one page more than fits
+    sh = _shape(prompt_len=pages * 256, resp_len=8)
+    pt = _table(num_pages=pages, num_splits=1, offs=[0, pages])
+    assert _fwd_noalloc(sh, pt) == WORKSPACE
+
+
 def test_prompt_free_table_needs_no_pools():
     """P = 0: no pages, pools may be NULL; validation passes up to the launch."""
     sh = _shape(prompt_len=0)
