@@ -20,7 +20,7 @@ prompt and response keys and values.
 """
 import os
 import time
-from concurrent.futures import ThreadPoolExecutor
+from concurrent.futures import ThreadPoolExecutor, as_completed
 
 import numpy as np
 import pytest
@@ -34,6 +34,17 @@ from response_replay_attention_amd import Member, PromptCache, replay_backward, 
 from tests.parity import assert_close, assert_lse_close
 
 pytestmark = pytest.mark.gpu
+
+_say = print
+
+
+@pytest.fixture(autouse=True)
+def _report_progress(progress):
+    """Every step of these tests reports to the terminal as it ends."""
+    global _say
+    _say = progress
+    yield
+    _say = print
 
 ROW_BLOCK = 32           # oracle rows per score block (bounds its temporaries)
 HOST_BUDGET = 150 << 30  # host bytes the oracle tasks of one test may hold at once
@@ -52,9 +63,12 @@ def run_tasks(fn, tasks, per_task, resident=0):
         1, min(len(os.sched_getaffinity(0)), 16, len(tasks),
                max(HOST_BUDGET - resident, per_task) // per_task)))
     t0 = time.time()
+    out = [None] * len(tasks)
     with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=workers) as ex:
-        out = list(ex.map(fn, tasks))
-    print(f"  {len(tasks)} oracle tasks on {workers} threads: {time.time() - t0:.0f} s", flush=True)
+        futs = {ex.submit(fn, t): i for i, t in enumerate(tasks)}
+        for n, f in enumerate(as_completed(futs), 1):
+            out[futs[f]] = f.result()
+            _say(f"  oracle task {n}/{len(tasks)} done, {time.time() - t0:.0f} s on {workers} threads")
     return out
 
 
@@ -69,7 +83,9 @@ def prompt_f64(inp, P, kv):
     """The logical prompt K, V of one KV head as float64 ``[1, P, d]``."""
     kp = logical_prompt(inp["k_pool"], inp["l2p"], P, kv_heads=[kv]).cpu()
     vp = logical_prompt(inp["v_pool"], inp["l2p"], P, kv_heads=[kv]).cpu()
-    return oracle.as_f64(kp), oracle.as_f64(vp)
+    out = oracle.as_f64(kp), oracle.as_f64(vp)
+    _say(f"  prompt of KV head {kv} gathered ({P} positions)")
+    return out
 
 
 def run(shape, inp, resp=None):
@@ -86,7 +102,9 @@ def run(shape, inp, resp=None):
 
 
 def host_outputs(fwd, dq, dk, dv):
-    return {"o": fwd.o.cpu(), "lse": fwd.lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+    out = {"o": fwd.o.cpu(), "lse": fwd.lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+    _say(f"  GPU outputs copied to the host (R = {dq.shape[1]})")
+    return out
 
 
 def oracle_rows(shape, prompts, resp, rows, g, kv):
@@ -133,7 +151,7 @@ def cpu_resp(resp):
                          ids=["shard_262k", "prefix_2m_s8"])
 def test_full_size_sampled_rows(shape, n_random):
     """Rows 0, R-1 and seeded rows of every query head of all four KV groups."""
-    print(f"case {shape.name} sampled rows", flush=True)
+    _say(f"case {shape.name} sampled rows")
     inp = make_inputs(shape, seed=20260001, device="cuda")
     got = host_outputs(*run(shape, inp)[1:])
     g = shape.hq // shape.hkv
@@ -146,14 +164,14 @@ def test_full_size_sampled_rows(shape, n_random):
                     resident=shape.hkv * 2 * shape.prompt_len * shape.head_dim * 8)
     for kv, (o_r, lse_r, dq_r) in enumerate(out):
         check_rows(f"kv{kv}", got, o_r, lse_r, dq_r, rows, range(kv * g, (kv + 1) * g))
-        print(f"  kv head {kv} ok", flush=True)
+        _say(f"  kv head {kv} ok")
 
 
 @pytest.mark.parametrize("shape", [FULL_2M, STRESS_4M], ids=["prefix_2m_s8", "stress_4m_s16"])
 def test_full_size_zero_query_closed_form(shape):
     """Q = 0 at full size: every row, every head.  LSE_i = ln(P + i + 1) and
     O_i = mean of the P + i + 1 visible values."""
-    print(f"case {shape.name} Q = 0", flush=True)
+    _say(f"case {shape.name} Q = 0")
     inp = make_inputs(shape, seed=20260003, device="cuda", q_zero=True)
     _, fwd, *_ = run(shape, inp)
     P, R, g = shape.prompt_len, shape.resp_len, shape.hq // shape.hkv
@@ -175,7 +193,7 @@ def test_full_size_peaked_scores():
     zero): rows 0, R-1 and seeded rows of every head of all four groups.  The
     outputs are O(0.1-1), so only the relative bounds apply."""
     shape = FULL_2M
-    print(f"case {shape.name} peaked", flush=True)
+    _say(f"case {shape.name} peaked")
     inp = make_inputs(shape, seed=20260006, device="cuda", q_mult=4.0)
     got = host_outputs(*run(shape, inp)[1:])
     g = shape.hq // shape.hkv
@@ -200,7 +218,7 @@ def test_full_size_late_dominant_keys_in_last_split():
     the softmax spreads over those 64 keys (not one-hot).  KV heads 0 and 1
     (normal scores) are checked on sampled rows with the relative bounds."""
     shape = FULL_2M
-    print(f"case {shape.name} late dominant keys", flush=True)
+    _say(f"case {shape.name} late dominant keys")
     inp = make_inputs(shape, seed=20260007, device="cuda")
     d, P = shape.head_dim, shape.prompt_len
     gen = torch.Generator().manual_seed(77)
@@ -258,15 +276,15 @@ def _every_head_64_rows(shape, members, got, inp, seed):
     t0 = time.time()
     for i, (ms, resp) in enumerate(members):
         check_kv_given_stats(f"R={ms.resp_len}", ms, resp, got[i])
-        print(f"  member R={ms.resp_len}: every head on 64 rows, every key of dK_r/dV_r ok", flush=True)
-    print(f"  dK_r/dV_r given the GPU's statistics: {time.time() - t0:.0f} s", flush=True)
+        _say(f"  member R={ms.resp_len}: every head on 64 rows, every key of dK_r/dV_r ok")
+    _say(f"  dK_r/dV_r given the GPU's statistics: {time.time() - t0:.0f} s")
 
 
 @pytest.mark.timeout(1200)
 def test_group_replay_every_head_64_rows():
     """G = 8 over the shared 2M prefix, replayed serially (R = 512 ... 4096)."""
     shape = GROUP_2M
-    print(f"case {shape.name} every head, 64 rows", flush=True)
+    _say(f"case {shape.name} every head, 64 rows")
     inp = make_inputs(shape, seed=20260004, device="cuda")
     lens = GROUP_2M_RESP_LENS
     resps = [make_response(shape.with_(resp_len=r), 100 + i, device="cuda") for i, r in enumerate(lens)]
@@ -288,7 +306,7 @@ def test_group_replay_every_head_64_rows():
 def test_stress_prefix_every_head_64_rows():
     """The 4,456,448-position prefix (17,408 pages, 16 splits), R = 2048."""
     shape = STRESS_4M
-    print(f"case {shape.name} every head, 64 rows", flush=True)
+    _say(f"case {shape.name} every head, 64 rows")
     inp = make_inputs(shape, seed=20260001, device="cuda")
     got = host_outputs(*run(shape, inp)[1:])
     _every_head_64_rows(shape, [(shape, cpu_resp(inp))], [got], inp, seed=600)
@@ -314,7 +332,7 @@ def test_group_peak_memory_follows_longest_member():
     torch.cuda.synchronize()
     peak_group = torch.cuda.max_memory_allocated() - base
     assert torch.cuda.memory_allocated() == base
-    print(f"peak longest {peak_longest / 2**20:.1f} MiB, group {peak_group / 2**20:.1f} MiB", flush=True)
+    _say(f"peak longest {peak_longest / 2**20:.1f} MiB, group {peak_group / 2**20:.1f} MiB")
     assert peak_group <= peak_longest + (1 << 20)
 
 
@@ -330,7 +348,7 @@ def test_full_size_every_row(shape):
     O, LSE and their contribution to dK_r and dV_r, and a KV head's dK_r /
     dV_r is the sum of those contributions over the heads of its group and all
     their rows."""
-    print(f"case {shape.name} every row", flush=True)
+    _say(f"case {shape.name} every row")
     inp = make_inputs(shape, seed=20260001, device="cuda")
     got = host_outputs(*run(shape, inp)[1:])
     g, P, R = shape.hq // shape.hkv, shape.prompt_len, shape.resp_len
@@ -367,6 +385,5 @@ def test_full_size_every_row(shape):
          "dK_r": assert_close("dK_r", got["dk"], dk_r),
          "dV_r": assert_close("dV_r", got["dv"], dv_r)}
     lse_rel = assert_lse_close("LSE", got["lse"], lse_r)
-    print(f"  LSE rel {lse_rel:.2e}; "
-          + "; ".join(f"{k} max_abs {v['max_abs']:.2e} rel_l2 {v['rel_l2']:.2e}" for k, v in m.items()),
-          flush=True)
+    _say(f"  LSE rel {lse_rel:.2e}; "
+          + "; ".join(f"{k} max_abs {v['max_abs']:.2e} rel_l2 {v['rel_l2']:.2e}" for k, v in m.items()))
