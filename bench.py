@@ -316,6 +316,10 @@ def main() -> int:
                          "(merged O and LSE per member, no backward)")
     ap.add_argument("--blocks", type=int, default=1,
                     help="replay the member as this many token blocks, last block first")
+    ap.add_argument("--late-dominant-keys", action="store_true",
+                    help="every query row points near one direction and the last 64 prompt keys "
+                         "of KV head 0 dominate it (the forward's exact recompute in the last "
+                         "split); not a headline workload")
     ap.add_argument("--identity-pages", action="store_true",
                     help="place logical page p in pool slot p instead of a seeded random slot")
     ap.add_argument("--copy-probe", action="store_true",
@@ -331,7 +335,7 @@ def main() -> int:
     import torch
 
     from replay_inputs import (CAPTURE_WORKLOADS, FULL_2M, GROUP_2M, GROUP_2M_RESP_LENS,
-                               WORKLOADS, make_inputs, make_response)
+                               WORKLOADS, make_inputs, make_response, plant_late_dominant_keys)
     if args.workload in CAPTURE_WORKLOADS:
         return bench_capture(args, CAPTURE_WORKLOADS[args.workload])
     from response_replay_attention_amd import (Member, PromptCache, block_bounds, ls_timing_enable,
@@ -347,6 +351,8 @@ def main() -> int:
     # every other workload is one member
     member_shapes = ([shape.with_(resp_len=r) for r in GROUP_2M_RESP_LENS] if group else [shape])
     inp = make_inputs(member_shapes[0], args.seed, device=dev, identity_pages=args.identity_pages)
+    if args.late_dominant_keys:
+        plant_late_dominant_keys(inp, member_shapes[0], args.seed, kv=0, n=64)
     members = [Member(inp["q"], inp["k_resp"], inp["v_resp"], inp["d_o"])]
     for i, sh in enumerate(member_shapes[1:], start=1):
         r = make_response(sh, args.seed + i, device=dev)
@@ -426,7 +432,8 @@ def main() -> int:
     digest = source_digest()
     # the counters were taken on the default workload (random page placement)
     traffic = (read_traffic(digest) if shape.name == FULL_2M.name and not args.score
-               and not args.identity_pages and not block_inputs else None)
+               and not args.identity_pages and not block_inputs and not args.late_dominant_keys
+               else None)
 
     out = {
         "metric": "replay-attn fwd+bwd TFLOP/s & prompt-keys/s at 2M prefix; % bf16 MFMA peak",
@@ -473,6 +480,8 @@ def main() -> int:
             "source": os.path.relpath(CLOCK_SUMMARY, ROOT)}
     if args.identity_pages:
         out["config"]["page_layout"] = "identity"
+    if args.late_dominant_keys:
+        out["config"]["inputs"] = "late dominant keys (last 64 prompt keys of KV head 0)"
     if block_inputs:
         out["config"]["token_blocks"] = [list(b) for b in bounds]
         out["config"]["mode"] = "reverse token-block replay"

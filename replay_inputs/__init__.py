@@ -225,6 +225,29 @@ def make_inputs(shape: ReplayShape, seed: int, device="cpu", *,
     return out
 
 
+def plant_late_dominant_keys(inp: Dict[str, torch.Tensor], shape: ReplayShape, seed: int,
+                             kv: int = 0, n: int = 64) -> None:
+    """Turn a problem drawn by :func:`make_inputs` into one whose last ``n``
+    prompt keys of KV head ``kv`` dominate every query row of that head, late
+    in the last split (in place).
+
+    Every query row becomes ``u + 0.1 q`` for one seeded direction ``u``
+    (``|u|^2 ~ d``), and keys ``P - n .. P - 1`` of KV head ``kv`` become
+    ``3u + 2 z`` (``z`` seeded N(0, 1)): with scale ``1/sqrt(d)`` they score
+    about ``3 sqrt(d)`` natural units, spread by about 2, while every other
+    key scores about N(0, 1).  The prompt must end on a page boundary and
+    ``n <= 256``.  Pure data generation: no attention arithmetic."""
+    d, P = shape.head_dim, shape.prompt_len
+    assert P % shape.page_size == 0 and 0 < n <= shape.page_size
+    g = _gen(seed, 14, "cpu")
+    u = torch.randn(d, generator=g).to(torch.bfloat16).float()
+    z = torch.randn(n, d, generator=g)
+    dev = inp["q"].device
+    inp["q"] = (u[None, None, :].to(dev) + 0.1 * inp["q"].float()).to(torch.bfloat16)
+    last = int(inp["l2p"][shape.num_pages - 1])          # pool slot of the last logical page
+    inp["k_pool"][last, kv, shape.page_size - n:] = (3.0 * u[None, :] + 2.0 * z).to(torch.bfloat16).to(dev)
+
+
 def make_response(shape: ReplayShape, seed: int, device="cpu") -> Dict[str, torch.Tensor]:
     """Only the response side of a problem (``q``, ``k_resp``, ``v_resp``,
     ``d_o``), drawn exactly as :func:`make_inputs` draws them: used for the

@@ -29,7 +29,8 @@ from threadpoolctl import threadpool_limits
 
 import oracle
 from replay_inputs import (FULL_2M, GROUP_2M, GROUP_2M_RESP_LENS, SHARD_256K, STRESS_4M,
-                           logical_prompt, make_inputs, make_response, sample_rows)
+                           logical_prompt, make_inputs, make_response, plant_late_dominant_keys,
+                           sample_rows)
 from response_replay_attention_amd import Member, PromptCache, replay_backward, replay_forward, replay_group
 from tests.parity import assert_close, assert_lse_close
 
@@ -221,12 +222,7 @@ def test_full_size_late_dominant_keys_in_last_split():
     _say(f"case {shape.name} late dominant keys")
     inp = make_inputs(shape, seed=20260007, device="cuda")
     d, P = shape.head_dim, shape.prompt_len
-    gen = torch.Generator().manual_seed(77)
-    u = torch.randn(d, generator=gen).to(torch.bfloat16).float()
-    inp["q"] = (u[None, None, :].cuda() + 0.1 * inp["q"].float()).to(torch.bfloat16)
-    last = int(inp["l2p"][shape.num_pages - 1])          # pool slot of the last logical page
-    noise = torch.randn(64, d, generator=gen)
-    inp["k_pool"][last, 0, 192:] = (3.0 * u[None, :] + 2.0 * noise).to(torch.bfloat16).cuda()
+    plant_late_dominant_keys(inp, shape, seed=77, kv=0, n=64)
     got = host_outputs(*run(shape, inp)[1:])
     g = shape.hq // shape.hkv
     rows = np.stack([pick_rows(shape.resp_len, 3, seed=200 + h) for h in range(shape.hq)])
