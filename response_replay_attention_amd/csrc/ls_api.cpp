@@ -286,6 +286,7 @@ ls_status ls::fwd_launch(const ls_attn_shape* sh, const ls_page_table* pt, int32
   r.slot_base = pt->num_splits;
   r.moffs = nmem > 1 ? moffs_dev : nullptr;
   r.nmembers = nmem;
+  r.lpt = (nmem <= 1 && sh->resp_len % kFwdRows == 0) ? 1 : 0;
   const int rgrid = sh->num_kv_heads * plan.mtiles;
   return run("fwd_resp", stream, [&] { return launch_fwd(r, d, true, rgrid, stream); });
 }
@@ -504,6 +505,7 @@ ls_status ls_replay_attn_bwd(const ls_attn_shape* sh, const ls_page_table* pt, c
   r.k = static_cast<const uint16_t*>(k_resp);
   r.v = static_cast<const uint16_t*>(v_resp);
   r.slot_base = plan.units;
+  r.lpt = (sh->resp_len % kBwdRows == 0) ? 1 : 0;
   const int rgrid = sh->num_kv_heads * plan.mtiles;
   st = run("bwd_resp_dq", stream, [&] { return launch_bwd_dq(r, d, true, rgrid, stream); });
   if (st != LS_OK) return st;

@@ -375,7 +375,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dq(const AttnArgs a) {
   const int w4 = wave & 3;
   const int hf = lane >> 5, lq = lane & 31;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w = RESP ? tile_item(a, kBwdRows, blockIdx.x, gridDim.x) : xcd_remap(blockIdx.x, gridDim.x);
   const int per_unit = a.mtiles * a.hkv;
   const int unit = w / per_unit;
   const int rem = w - unit * per_unit;

@@ -418,6 +418,20 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * q + (x < r ? x : r) + s;
 }
 
+// Work item of workgroup `bid` for a launch over (KV head, row tile) items,
+// item index = kv * mtiles + mtile.  Normally the XCD-aware remap above.  For
+// the causal response block (lpt) every tile stays inside one query head and
+// tile t of a head sees t + 1 tiles' worth of keys, so the items go out
+// longest first: workgroup i takes tile t = T-1 - i / (Hkv*g) of head-slot
+// i % (Hkv*g).  The hardware deals workgroup i to XCD i % 8, so every XCD
+// gets the same mix of lengths, each in decreasing order.  Bijective.
+__device__ __forceinline__ int tile_item(const AttnArgs& a, int rows_per_tile, int bid, int n) {
+  if (!a.lpt) return xcd_remap(bid, n);
+  const int g = a.hq / a.hkv, heads = a.hkv * g, T = a.R / rows_per_tile;
+  const int t = T - 1 - bid / heads, r = bid - (bid / heads) * heads;
+  return (r / g) * a.mtiles + (r % g) * T + t;
+}
+
 // max of x over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the two
 // half-waves in registers (no LDS traffic); for lane l < 32 the partner value
 // comes back in the second result, for l >= 32 in the first.

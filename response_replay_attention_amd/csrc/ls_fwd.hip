@@ -44,17 +44,17 @@ namespace ls {
 // block's max when `first`), so the softmax needs no per-block maximum: the
 // lane's running maximum of raw scores (mlane) is checked against the shift
 // once the range is done.
-// MASK: keys at index >= nvalid, and (response block) keys before kmin or
-// after kmax (block-relative: the row's member start and its own position)
-// are masked; COPY: issue the block copies.
+// MASK: only the keys at row offsets lo..hi of the lane's own key rows are
+// visible (lane rows 4*hf + 8*(r/4) + r%4 of the block; the caller folds the
+// block's valid length, the row's own position and its member start into the
+// two per-lane thresholds); COPY: issue the block copies.
 template <int D, bool MASK, bool COPY>
 __device__ __forceinline__ void fwd_step(const LanesCM<D>& tl, const BlockLoaderCM<D, kFwdWaves>& ldr,
                                          const uint16_t* kt, const uint16_t* vt,
                                          const bf16x8 (&qr)[D / 16], f32x16 (&acc)[D / 32],
                                          float s2, bool first, float& mu, float& mlane,
                                          float& lsum, uint32_t kdst, i32x4 kdesc, uint32_t vdst,
-                                         i32x4 vdesc, int nvalid = kBN, int kmax = 0x7fffffff,
-                                         int hf = 0, int kmin = -0x7fffffff) {
+                                         i32x4 vdesc, int hi = kBN, int lo = 0) {
   constexpr int NS = D / 16;   // score MFMAs per step = PV MFMAs per step
   constexpr int NMT = D / 32;  // 32-wide d tiles of O^T
   constexpr int PF = 2;        // LDS prefetch distance, in MFMAs (3 spills in the loop)
@@ -84,11 +84,8 @@ __device__ __forceinline__ void fwd_step(const LanesCM<D>& tl, const BlockLoader
   }
   __builtin_amdgcn_s_setprio(0);
   if (MASK) {
-    // key crow(r, hf) = 4*hf + 8*(r/4) + r%4 of the block is visible iff
-    // kmin <= key <= min(nvalid - 1, kmax); compared as compile-time row
-    // offsets against per-lane thresholds, so no key index is kept in a register
-    const int hi = min(nvalid - 1, kmax) - 4 * hf;
-    const int lo = max(kmin, -0x7fff) - 4 * hf;
+    // compile-time row offsets against the per-lane thresholds, so no key
+    // index is kept in a register
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = 8 * (r >> 2) + (r & 3);
@@ -143,7 +140,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, lq = lane & 31;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w = RESP ? tile_item(a, kFwdRows, blockIdx.x, gridDim.x) : xcd_remap(blockIdx.x, gridDim.x);
   const int per_unit = a.mtiles * a.hkv;
   const int unit = w / per_unit;
   const int rem = w - unit * per_unit;
@@ -165,7 +162,11 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   // group are computed on a copy of its last row and never stored.
   bf16x8 qr[D / 16];
   const int qi = m % a.R;
-  const int qlo = RESP ? member_start(a, qi) : 0;  // first visible response key
+  // masked blocks: the row sees response keys [member start, qoff + qi]; as
+  // thresholds relative to the lane's first key row 4*hf (keys past the
+  // block's valid rows lie beyond qoff + qi, so the bounds cover them)
+  const int lane_hi = RESP ? qi + a.qoff - 4 * hf : -4 * hf;
+  const int lane_lo = RESP ? member_start(a, qi) - 4 * hf : -4 * hf;
   {
     const uint16_t* qp = a.q + (row0 + min(m, GR - 1)) * D + 8 * hf;
 #pragma unroll
@@ -261,27 +262,57 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
       __syncthreads();
     }
 
-    // ---- masked blocks (partial last prompt page; the causal response block)
+    // ---- masked blocks (partial last prompt page; the causal response
+    // block) through the same 4-stage ring, three blocks ahead: step j waits
+    // for block j, starts the copies of block j+3 into the stage block j-1
+    // used and computes block j.  Every step issues one block's copies (a
+    // block past the range gets a zero-length copy, which reads nothing and
+    // is never computed), so "at most two blocks in flight" is a fixed vmcnt.
     {
       float mlane = -kInf;
-      for (int j = max(nfull, walk.jfirst); j < nblocks; ++j) {
-        int nv, key0;
-        const size_t off = walk.block(j, nv, key0);
-        if (nv > 0) {
-          load_block_cm<false>(ldr, k0, a.k + off, nv);
-          load_block_cm<true>(ldr, v0, a.v + off, nv);
-        }
+      int jb = max(nfull, walk.jfirst);
+      // opaque per pass, so that the block addresses below are computed here
+      // rather than hoisted out of the pass loop and kept live across it
+      asm volatile("" : "+s"(jb));
+      if (jb < nblocks) {
+        // Q and any reloaded lane thresholds have landed: the compiler then
+        // has no load of its own pending in the loop and adds no wait there
+        // that would drain the copies
+        asm volatile("" ::"v"(lane_hi), "v"(lane_lo));
         wait_loads_le<0>();
-        __syncthreads();
-        if (nv > 0) {
-          tl.refresh();
-          const i32x4 none = {0, 0, 0, 0};
-          fwd_step<D, true, false>(tl, ldr, k0, v0, qr, acc, a.s2, pass0 && mref == -kInf, mref,
-                                   mlane, lsum, 0, none, 0, none, nv,
-                                   RESP ? qi + a.qoff - key0 : 0x7fffffff, hf,
-                                   RESP ? qlo - key0 : -0x7fffffff);
+#define LS_ISSUE(J)                                                                       \
+  {                                                                                       \
+    const int s_ = ((J) - jb) & (NST - 1);                                                \
+    int nv_ = 0, key0_ = 0;                                                               \
+    const size_t off_ = (J) < nblocks ? walk.block((J), nv_, key0_) : 0;                  \
+    /* the clamp may be done on the vector unit: bring it back to a scalar */            \
+    nv_ = __builtin_amdgcn_readfirstlane(max(nv_, 0));                                    \
+    load_block_cm<false>(ldr, s_ == 0 ? k0 : s_ == 1 ? k1 : s_ == 2 ? k2 : k3, a.k + off_, \
+                         nv_);                                                            \
+    load_block_cm<true>(ldr, s_ == 0 ? v0 : s_ == 1 ? v1 : s_ == 2 ? v2 : v3, a.v + off_,  \
+                        nv_);                                                             \
+  }
+        LS_ISSUE(jb)
+        LS_ISSUE(jb + 1)
+        LS_ISSUE(jb + 2)
+        for (int j = jb; j < nblocks; ++j) {
+          ring_barrier<2 * NLD>();  // block j landed; the stage of block j-1 is free
+          LS_ISSUE(j + 3)
+          const int s = (j - jb) & (NST - 1);
+          int nv, key0;
+          walk.block(j, nv, key0);
+          if (nv > 0) {
+            tl.refresh();
+            const i32x4 none = {0, 0, 0, 0};
+            fwd_step<D, true, false>(tl, ldr, s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3,
+                                     s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3, qr, acc,
+                                     a.s2, pass0 && mref == -kInf, mref, mlane, lsum, 0, none, 0,
+                                     none, RESP ? lane_hi - key0 : lane_hi + nv - 1,
+                                     lane_lo - key0);
+          }
         }
-        __syncthreads();  // tiles are rewritten by the next block
+#undef LS_ISSUE
+        wait_loads_le<0>();  // no copy into LDS outlives the loop
       }
       const float mb = wave_max_halves(mlane) * a.s2;
       mtrue = fmaxf(mtrue, mb);

@@ -39,6 +39,10 @@ struct AttnArgs {
   // j <= qoff + i; k/v (response) and dk/dv have kvr rows per KV head, of
   // which the first RK = qoff + R are used; kv_accum: dk/dv += instead of =
   int32_t qoff, RK, kvr, kv_accum;
+  // causal response block whose tiles each stay inside one query head (R a
+  // multiple of the tile rows, one member): dispatch the tiles longest key
+  // range first (lpt != 0)
+  int32_t lpt;
   float s2;               // scale * log2(e)
   float scale;
   // forward outputs (slot arrays): o [slots, Hq*R, d], m/l [slots, Hq*R]
