@@ -48,6 +48,7 @@ KERNELS = ("fwd_prompt", "fwd_combine", "fwd_resp", "lse_merge", "bwd_dot", "bwd
            "bwd_resp_dq", "bwd_resp_dkdv", "kv_reduce", "dq_reduce", "page_append")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_prompt_dq_traffic_prefix2M.md")
 CLOCK_SUMMARY = os.path.join(ROOT, "profiles", "prompt_kernels_clock_lds_prefix2M.md")
+GEMM_SUMMARY = os.path.join(ROOT, "profiles", "library_gemm_bf16_ceiling.md")
 NOMINAL_CLOCK_GHZ = 2.4     # the clock of the published peak (256 CU x 4 SIMD x 1024 flop/clk)
 
 
@@ -109,6 +110,15 @@ def measured_clock_ghz(kernel: str):
     summary (GRBM_GUI_ACTIVE per XCD over the dispatch's duration), or None."""
     try:
         return float(summary_values(CLOCK_SUMMARY)[f"{kernel}_clock_ghz"])
+    except (KeyError, ValueError):
+        return None
+
+
+def library_gemm_tflops():
+    """Sustained rate of the vendor library's square bf16 GEMM on this part
+    (`bench.py --library-gemm`) from the committed summary, or None."""
+    try:
+        return float(summary_values(GEMM_SUMMARY)["library_gemm_tflops"])
     except (KeyError, ValueError):
         return None
 
@@ -214,6 +224,43 @@ def cpu_baseline_capture(shape, inp):
                    f"positions) over every earlier position of the {T}-position prompt; "
                    f"{secs:.1f} s compute (+{t1 - t0:.1f} s to gather inputs)"),
     }
+
+
+def bench_library_gemm(args) -> int:
+    """Calibration, not the workload: the vendor library's dense bf16 GEMM
+    (torch.matmul, which dispatches to hipBLASLt) on square operands, timed
+    with HIP events on the current stream.  Its sustained rate is the
+    practical MFMA ceiling of the part: the clock it holds under a full
+    matrix load is below the 2.4 GHz of the published peak."""
+    import torch
+    torch.manual_seed(args.seed)
+    dev = torch.device("cuda:0")
+    res = {}
+    for n, iters in ((8192, 50), (16384, 8)):
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        res[str(n)] = {"ms": round(ms, 4), "tflops": round(2.0 * n ** 3 / ms / 1e9, 1)}
+        print(f"gemm {n}^3 bf16: {ms:.3f} ms, {res[str(n)]['tflops']} TFLOP/s", file=sys.stderr,
+              flush=True)
+        del a, b, c
+    best = max(v["tflops"] for v in res.values())
+    print(json.dumps({
+        "metric": "library dense bf16 GEMM TFLOP/s (calibration)", "value": best,
+        "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic", "config": {"workload": "torch.matmul square bf16", "sizes": res},
+        "frac_of_bf16_peak": round(best / PEAK_BF16_TFLOPS, 4)}), flush=True)
+    return 0
 
 
 def bench_capture(args, shape) -> int:
@@ -324,6 +371,9 @@ def main() -> int:
                     help="place logical page p in pool slot p instead of a seeded random slot")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="calibration only: time the vendor library's square bf16 GEMM "
+                         "(the practical MFMA ceiling) instead of a workload")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -331,6 +381,9 @@ def main() -> int:
               "(see DESIGN.md for how the splits would shard over CP ranks); run with --gpus 1",
               file=sys.stderr)
         return 2
+
+    if args.library_gemm:
+        return bench_library_gemm(args)
 
     import torch
 
@@ -478,6 +531,13 @@ def main() -> int:
             "clock_ghz": clk, "peak": round(PEAK_BF16_TFLOPS * clk / NOMINAL_CLOCK_GHZ, 1),
             "frac": round(achieved / (PEAK_BF16_TFLOPS * clk / NOMINAL_CLOCK_GHZ), 4),
             "source": os.path.relpath(CLOCK_SUMMARY, ROOT)}
+    gemm = library_gemm_tflops()
+    if gemm:
+        # the same kernel against what the vendor's own bf16 GEMM sustains here
+        out["frac_of_library_gemm"] = {
+            "library_gemm_tflops": gemm, "frac": round(achieved / gemm, 4),
+            "step_frac": round(tflops / gemm, 4),
+            "source": os.path.relpath(GEMM_SUMMARY, ROOT)}
     if args.identity_pages:
         out["config"]["page_layout"] = "identity"
     if args.late_dominant_keys:
