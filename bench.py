@@ -377,8 +377,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how the splits would shard over CP ranks); run with --gpus 1",
+        print("bench.py measures one GPU: the library has no multi-GPU path (its page splits "
+              "stand in for the context-parallel ranks on one device); run with --gpus 1",
               file=sys.stderr)
         return 2
 
