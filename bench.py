@@ -49,6 +49,7 @@ KERNELS = ("fwd_prompt", "fwd_combine", "fwd_resp", "lse_merge", "bwd_dot", "bwd
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_prompt_dq_traffic_prefix2M.md")
 CLOCK_SUMMARY = os.path.join(ROOT, "profiles", "prompt_kernels_clock_lds_prefix2M.md")
 GEMM_SUMMARY = os.path.join(ROOT, "profiles", "library_gemm_bf16_ceiling.md")
+PROBE_SUMMARY = os.path.join(ROOT, "profiles", "mfma_calibration_probes.md")
 NOMINAL_CLOCK_GHZ = 2.4     # the clock of the published peak (256 CU x 4 SIMD x 1024 flop/clk)
 
 
@@ -66,13 +67,14 @@ def flops(shape) -> dict:
 def source_digest() -> str:
     """Hash of the kernel sources with comments and blank space taken out, so
     that a counter summary stays attached to the code it measured across
-    edits that change no code."""
+    edits that change no code.  The calibration probe (ls_calib.hip) is not
+    part of the measured path and is left out."""
     import re
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "response_replay_attention_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")) and name != "ls_calib.hip":
             with open(os.path.join(csrc, name)) as f:
                 text = f.read()
             text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -110,6 +112,16 @@ def measured_clock_ghz(kernel: str):
     summary (GRBM_GUI_ACTIVE per XCD over the dispatch's duration), or None."""
     try:
         return float(summary_values(CLOCK_SUMMARY)[f"{kernel}_clock_ghz"])
+    except (KeyError, ValueError):
+        return None
+
+
+def lds_fed_mfma_tflops():
+    """Sustained rate of the calibration probe whose MFMAs take their A
+    operand from LDS at the attention kernels' ratio (`bench.py
+    --mfma-probe`, mode 2) from the committed summary, or None."""
+    try:
+        return float(summary_values(PROBE_SUMMARY)["lds_fed_mfma_tflops"])
     except (KeyError, ValueError):
         return None
 
@@ -263,6 +275,47 @@ def bench_library_gemm(args) -> int:
     return 0
 
 
+def bench_mfma_probe(args) -> int:
+    """Calibration, not the workload: the library's MFMA probe
+    (ls_calib_mfma) in its four modes, 2048 workgroups of 512 threads, three
+    timed launches each after one warm-up launch, HIP events on the current
+    stream.  Register operands give the rate the part sustains on the matrix
+    units alone under its power limit; LDS operands at the attention kernels'
+    1 KiB per 32768 flop add the cost of their operand stream."""
+    import torch
+
+    from response_replay_attention_amd import ls_calib_mfma
+    dev = torch.device("cuda:0")
+    wgs, iters = 2048, 100_000
+    out_t = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    names = {0: "32x32x16 bf16, register operands", 1: "16x16x32 bf16, register operands",
+             2: "32x32x16 bf16, A from LDS (1 KiB per MFMA)",
+             3: "16x16x32 bf16, A from LDS (1 KiB per two MFMAs)"}
+    res = {}
+    for mode, name in names.items():
+        ls_calib_mfma(mode, wgs, 8, out_t)
+        rates = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fl = ls_calib_mfma(mode, wgs, iters, out_t)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            rates.append(fl / ms / 1e9)
+            print(f"mode {mode} ({name}): {ms:.2f} ms, {rates[-1]:.1f} TFLOP/s", file=sys.stderr,
+                  flush=True)
+        res[str(mode)] = {"probe": name, "tflops": round(max(rates), 1),
+                          "tflops_all": [round(r, 1) for r in rates]}
+    print(json.dumps({
+        "metric": "MFMA calibration probe TFLOP/s (power-limited ceiling)",
+        "value": res["2"]["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "ls_calib_mfma", "workgroups": wgs, "steps": iters, "modes": res}}),
+        flush=True)
+    return 0
+
+
 def bench_capture(args, shape) -> int:
     import torch
 
@@ -374,6 +427,9 @@ def main() -> int:
     ap.add_argument("--library-gemm", action="store_true",
                     help="calibration only: time the vendor library's square bf16 GEMM "
                          "(the practical MFMA ceiling) instead of a workload")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="calibration only: the MFMA rate the part sustains under its power "
+                         "limit, with register operands and with an LDS operand stream")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -384,6 +440,8 @@ def main() -> int:
 
     if args.library_gemm:
         return bench_library_gemm(args)
+    if args.mfma_probe:
+        return bench_mfma_probe(args)
 
     import torch
 
@@ -538,6 +596,13 @@ def main() -> int:
             "library_gemm_tflops": gemm, "frac": round(achieved / gemm, 4),
             "step_frac": round(tflops / gemm, 4),
             "source": os.path.relpath(GEMM_SUMMARY, ROOT)}
+    probe = lds_fed_mfma_tflops()
+    if probe:
+        # against the MFMA rate the part sustains with an LDS operand stream of
+        # the same bytes per flop (no softmax, copies or barriers)
+        out["frac_of_lds_fed_mfma_probe"] = {
+            "probe_tflops": probe, "frac": round(achieved / probe, 4),
+            "source": os.path.relpath(PROBE_SUMMARY, ROOT)}
     if args.identity_pages:
         out["config"]["page_layout"] = "identity"
     if args.late_dominant_keys:

@@ -336,6 +336,26 @@ ls_status ls_timing_enable(int32_t on);
 ls_status ls_timing_reset(void);
 ls_status ls_timing_read(const char* kernel, int32_t* launches, double* total_ms);
 
+/* MFMA calibration probe (measurement aid, not part of the method).  Runs
+ * `workgroups` workgroups of 512 threads (two waves per SIMD), each wave doing
+ * `iters` steps of 4 x 32768 bf16 flop, with random operands cycled every
+ * MFMA and no global memory traffic but one float per thread stored to `out`:
+ *   mode 0: v_mfma_f32_32x32x16_bf16, register operands;
+ *   mode 1: v_mfma_f32_16x16x32_bf16, register operands;
+ *   mode 2: 32x32x16 with the A operand read from LDS, 1 KiB per MFMA (the
+ *           attention kernels' ratio of LDS bytes to flops);
+ *   mode 3: 16x16x32 with the A operand read from LDS, one read per two MFMAs
+ *           (the same bytes per flop).
+ * Timed by the caller (events on `stream`), it gives the rate the part
+ * sustains under its power limit with and without an LDS operand stream.
+ *   out       device float [workgroups * 512], written (values meaningless).
+ *   flops     host: set to the floating-point operations of the launch.
+ * LS_ERR_INVALID_ARG for mode outside 0..3, workgroups < 1, iters < 8 or not
+ * a multiple of 8, or a null pointer (nothing launched); LS_ERR_HIP if the
+ * launch fails. */
+ls_status ls_calib_mfma(int32_t mode, int32_t workgroups, int32_t iters, float* out,
+                        double* flops, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     LsError,
     PageTable,
     lib,
+    ls_calib_mfma,
     ls_kv_page_append,
     ls_kv_page_table,
     ls_lse_merge,

@@ -32,7 +32,7 @@ EXPORTS = (
     "ls_replay_attn_fwd", "ls_replay_attn_fwd_members", "ls_replay_attn_fwd_noalloc",
     "ls_kv_page_append", "ls_lse_merge",
     "ls_replay_attn_bwd",
-    "ls_timing_enable", "ls_timing_reset", "ls_timing_read",
+    "ls_timing_enable", "ls_timing_reset", "ls_timing_read", "ls_calib_mfma",
 )
 
 
@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
         "ls_timing_enable": (I32, [I32]),
         "ls_timing_reset": (I32, []),
         "ls_timing_read": (I32, [ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_double)]),
+        "ls_calib_mfma": (I32, [I32, I32, I32, P, ctypes.POINTER(ctypes.c_double), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(h, name)
@@ -327,3 +328,14 @@ def ls_timing_read(kernel: str) -> Tuple[int, float]:
     ms = ctypes.c_double(0.0)
     _check("ls_timing_read", lib().ls_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def ls_calib_mfma(mode: int, workgroups: int, iters: int, out: torch.Tensor, stream=None) -> float:
+    """Launch the MFMA calibration probe; returns the launch's flops.  `out`
+    is a float32 device tensor of at least workgroups * 512 elements."""
+    _expect_at_least(out, int(workgroups) * 512, "out")
+    flops = ctypes.c_double(0.0)
+    _check("ls_calib_mfma", lib().ls_calib_mfma(int(mode), int(workgroups), int(iters),
+                                                _ptr(out, torch.float32, "out"),
+                                                ctypes.byref(flops), _stream(stream)))
+    return float(flops.value)

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libls_replay.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["ls_fwd.hip", "ls_bwd.hip", "ls_merge.hip", "ls_static.hip", "ls_api.cpp"]
+SOURCES = ["ls_fwd.hip", "ls_bwd.hip", "ls_merge.hip", "ls_static.hip", "ls_calib.hip", "ls_api.cpp"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -279,6 +279,16 @@ def test_timing_read_unknown_kernel_is_empty():
     assert rra.ls_timing_read("no_such_kernel") == (0, 0.0)
 
 
+def test_calib_probe_rejects_bad_arguments_before_any_launch():
+    f = ctypes.c_double(-1.0)
+    call = rra.lib().ls_calib_mfma
+    for mode, wgs, iters in ((4, 1, 8), (-1, 1, 8), (0, 0, 8), (0, 1, 4), (0, 1, 12)):
+        assert call(mode, wgs, iters, FAKE, ctypes.byref(f), None) == INVALID
+    assert call(0, 1, 8, None, ctypes.byref(f), None) == INVALID
+    assert call(0, 1, 8, FAKE, None, None) == INVALID
+    assert f.value == -1.0  # nothing was computed or launched
+
+
 def _fwd_members(sh, pt, offs, dev=FAKE, num_members=None, **ptrs):
     p = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, k_resp=FAKE, v_resp=FAKE, part_o=FAKE,
              part_m=FAKE, part_l=FAKE, ws=FAKE, ws_bytes=1 << 40)
