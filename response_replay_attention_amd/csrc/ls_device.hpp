@@ -1,6 +1,6 @@
 // Device helpers for the gfx950 kernels: bf16 MFMA operand types, the
-// 32x32x16 (backward) and 16x16x32 (forward) MFMAs, operand/accumulator lane
-// layouts, and the XCD-aware workgroup remap.
+// 32x32x16 MFMA, operand/accumulator lane layouts, and the XCD-aware
+// workgroup remap.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -130,52 +130,37 @@ struct Lanes32 {
   }
 };
 
-// ---- 16x16x32 forward operands (v_mfma_f32_16x16x32_bf16: D[16x16] +=
-// A[16x32] B[32x16]; lane l, n = l % 16, G = l / 16: A row n, k = 8G + j;
-// B column n, k = 8G + j; D rows 4G + r, column n, r = 0..3).
-//
-// The forward's K and V tiles are chunk-major: K keeps the 16-byte chunk c
-// (elements [8c, 8c+8)) of key row r in 16-byte slot 32c + r; V keeps chunk c
-// of row r in slot 32c + (r ^ 8*(c & 1)).  A wave owns 32 queries as two
-// halves qh of 16; per block it reads
-//   K fragment f = 2kk + kh: K[16kh + n][32kk + 8G + j], one 16-byte read at
-//     kb + 2048*kk + 256*kh (each fragment serves both query halves);
-//   V^T fragment dt: V[kappa(G, j)][16dt + n] with kappa(G, j) = 16*(j / 4) +
-//     4G + j % 4 -- the eight keys whose scores this lane holds, so P^T can be
-//     the B operand straight from the score registers -- two transpose reads
-//     at vb + 1024*dt (+256 for keys 16..31).
-// ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a group receives,
-// as element e, the 16-bit word (i & 3) of the 8 bytes addressed by lane
-// 4*e + (i >> 2) of the same group; so lane s of group G addresses row
-// 4G + (s >> 2) (+16), columns 16dt + 4*(s & 3) + [0, 4).
-// Every read is a per-lane base register plus an immediate, and both patterns
-// are free of LDS bank conflicts (64 banks of 4 bytes; the values and the bank
-// pattern were checked on the CPU for every lane and read, together with the
-// copies, at d = 128 and 256).
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
+// Forward tiles in chunk-major layouts.  K keeps the 16-byte chunk c (elements
+// [8c, 8c+8)) of key row r in 16-byte slot c*32 + r; V keeps chunk C of row r
+// in slot C*32 + (r ^ 4*(C & 3)).  With these, every operand read is one
+// per-lane base register plus an immediate, so no address arithmetic sits
+// between an MFMA and the read it waits for:
+//   K row read, k-step kk:            kb + 1024*kk bytes
+//   V transposed read (ks, mt, half): vb[half] + 2048*mt + 256*ks bytes
+// and both are free of LDS bank conflicts for their own read pattern (64 banks
+// of 4 bytes; checked on the CPU for every lane and read, together with the
+// copies, at d = 128 and 256).  The registers the reads fill are the same as
+// with the row-major swizzled tiles (row8 / col8 above).
 template <int D>
-struct Lanes16 {
-  int kb, vb;  // byte offsets inside a tile
-  __device__ __forceinline__ explicit Lanes16(int lane) {
-    const int s = lane & 15, G = lane >> 4, h = (s >> 1) & 1;
-    kb = 512 * G + 16 * s;
-    vb = 512 * h + 16 * ((4 * G + (s >> 2)) ^ (8 * h)) + 8 * (s & 1);
+struct LanesCM {
+  int kb, vb0, vb1;  // byte offsets inside a tile
+  __device__ __forceinline__ LanesCM(int hf, int lq) {
+    kb = 512 * hf + 16 * lq;
+    const int L = lq & 15, g1 = lq >> 4, q = 2 * g1 + ((L >> 1) & 1);
+    vb0 = 512 * q + 16 * ((4 * hf + (L >> 2)) ^ (4 * q)) + 8 * (L & 1);
+    vb1 = 512 * q + 16 * ((8 + 4 * hf + (L >> 2)) ^ (4 * q)) + 8 * (L & 1);
   }
-  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(kb), "+v"(vb)); }
-  __device__ __forceinline__ bf16x8 krow(const uint16_t* tile, int f) const {
+  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(kb), "+v"(vb0), "+v"(vb1)); }
+  __device__ __forceinline__ bf16x8 row8(const uint16_t* tile, int kk) const {
     return __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(tile) + kb +
-                                                2048 * (f >> 1) + 256 * (f & 1)));
+        bf16x8, *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(tile) + kb + 1024 * kk));
   }
-  __device__ __forceinline__ bf16x8 vcol(const uint16_t* tile, int dt) const {
+  __device__ __forceinline__ bf16x8 col8(const uint16_t* tile, int ks, int mt) const {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const char* base = reinterpret_cast<const char*>(tile) + vb + 1024 * dt;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 256));
+    const char* base = reinterpret_cast<const char*>(tile) + 2048 * mt + 256 * ks;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + vb0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + vb1));
     const s16x4 v[2] = {lo, hi};
     u16x8 r;
 #pragma unroll
@@ -255,11 +240,12 @@ __device__ __forceinline__ void load_block(const BlockLoader<D, NW>& L, uint16_t
   for (int j = 0; j < BlockLoader<D, NW>::NIW; ++j) copy16_to_lds(base + j * 1024, L.voff[j], desc);
 }
 
-// Copies of [32][D] bf16 blocks into the chunk-major tiles of Lanes16, spread
+// Copies of [32][D] bf16 blocks into the chunk-major tiles of LanesCM, spread
 // over NW waves: copy instruction j of wave w fills slots (w*NIW + j)*64 + lane,
 // so lane (hl = lane / 32) reads the 16 bytes of chunk c = 2*(w*NIW + j) + hl of
-// row lane % 32 (K; V: of row (lane % 32) ^ 8*hl, as c & 1 = hl).  Copy j adds
-// 32*j bytes (the next chunk pair) to the source offsets of copy 0.
+// row lane % 32 (K; V: of row (lane % 32) ^ 4*(c & 3)).  The source offsets of
+// copy 0 are kept; copy j adds 32*j bytes (the next chunk pair), and for V an
+// odd j also flips row bit 3 (c & 3 differs by 2).
 template <int D, int NW>
 struct BlockLoaderCM {
   static constexpr int NIW = (kBN * D * 2 / 1024) / NW;  // wave instructions per block
@@ -270,10 +256,10 @@ struct BlockLoaderCM {
       : lds0(__builtin_amdgcn_readfirstlane(wave) * NIW * 1024) {
     const int hl = lane >> 5;
     vk = (lane & 31) * 2 * D + 16 * hl + 32 * wave * NIW;
-    vv = vk ^ (16 * D * hl);
+    vv = vk ^ (8 * D * ((wave * NIW * 2 + hl) & 3));
   }
   __device__ __forceinline__ int koff(int j) const { return vk + 32 * j; }
-  __device__ __forceinline__ int voff(int j) const { return vv + 32 * j; }
+  __device__ __forceinline__ int voff(int j) const { return ((j & 1) ? (vv ^ (16 * D)) : vv) + 32 * j; }
   // copy instruction c of a step: K pieces first, then V
   __device__ __forceinline__ void issue(int c, uint32_t kdst, i32x4 kdesc, uint32_t vdst,
                                         i32x4 vdesc) const {
@@ -446,15 +432,13 @@ __device__ __forceinline__ int tile_item(const AttnArgs& a, int rows_per_tile, i
   return (r / g) * a.mtiles + (r % g) * T + t;
 }
 
-// max / sum of x over the four lanes that hold the same query column of a
-// 16x16 accumulator (l, l ^ 16, l ^ 32, l ^ 48)
-__device__ __forceinline__ float quad_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+// max of x over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the two
+// half-waves in registers (no LDS traffic); for lane l < 32 the partner value
+// comes back in the second result, for l >= 32 in the first.
+__device__ __forceinline__ float wave_max_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 }  // namespace ls

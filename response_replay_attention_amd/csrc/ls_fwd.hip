@@ -11,23 +11,19 @@
 // KV-head group):
 //   * the query heads of a KV group are packed into the M dimension, so every
 //     K/V byte staged in LDS serves 256 query rows;
-//   * each wave owns 32 query rows as two halves of 16; its Q stays in
-//     registers as the B operand;
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows read from LDS, each
-//     read serving both query halves) puts two queries and 8 of the block's 32
-//     keys per lane in registers, so a query's statistics are spread over the
-//     four lanes l, l^16, l^32, l^48;
+//   * each wave owns 32 query rows; its Q stays in registers as the B operand;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows read from LDS) puts
+//     one query per lane and 16 of the block's 32 keys per lane in registers,
+//     so the softmax statistics need one exchange between lanes l and l^32;
 //   * P^T (bf16) is the B operand of O^T = V^T P^T straight from registers; the
-//     V^T operand comes from the V tile by transpose reads gathering exactly
-//     the keys a lane holds; O^T keeps the lane's two queries, so the shifts
-//     and the final 1/l are per-lane scalars;
-//   * K and V tiles are stored chunk-major (Lanes16), so each operand read is
-//     a base register plus an immediate;
+//     V^T operand comes from the V tile by transpose reads; O^T keeps one query
+//     per lane, so the shift and the final 1/l are per-lane scalars;
+//   * K and V tiles are stored chunk-major (LanesCM), so each operand read is
+//     a base register plus an immediate offset;
 //   * full prompt blocks stream through a 4-stage LDS ring filled by
 //     buffer->LDS copies issued three blocks ahead; the second wave on each
 //     SIMD covers one wave's waits.  Masked blocks (the partial last prompt
-//     page, the causal response block) go through the same ring in a loop of
-//     their own;
+//     page, the causal response block) take a simple loop of their own;
 //   * the exp2 shift is fixed at the first block's max instead of following
 //     the running max, so no accumulator is ever rescaled; an input whose
 //     scores later exceed the shift by more than 2^32 is detected and its key
@@ -40,108 +36,95 @@ namespace ls {
 // mu) on the VALU, O^T += V(b)^T P(b), and the copies of block b+3.  Two
 // waves share each SIMD, so the hardware interleaves one wave's LDS waits
 // with the other's MFMAs; inside a wave the step is still a fixed sequence of
-// sched_barrier-fenced micro-segments (one operand read, the two MFMAs of
-// the fragment PF reads earlier, one copy instruction every CEV PV fragments),
-// which keeps the wave's LDS read stream steady.
+// sched_barrier-fenced micro-segments (one MFMA, the LDS read its MFMA PF
+// segments later needs, one copy instruction every CEV PV MFMAs), which keeps
+// the wave's LDS read stream steady.
 //
-// The wave's 32 queries are two halves qh of 16 (v_mfma_f32_16x16x32_bf16);
-// lane l (n = l % 16, G = l / 16) holds S^T[16kh + 4G + r][16qh + n], i.e. two
-// queries and eight of the block's keys, and every statistic is per (lane, qh).
 // The exp2 shift mu is fixed for the whole key range (set from the first
-// block's max when first[qh]), so the softmax needs no per-block maximum: the
+// block's max when `first`), so the softmax needs no per-block maximum: the
 // lane's running maximum of raw scores (mlane) is checked against the shift
 // once the range is done.
 // MASK: only the keys at row offsets lo..hi of the lane's own key rows are
-// visible (rows 4G + 16kh + r of the block; the caller folds the block's
-// valid length, the row's own position and its member start into per-lane
-// thresholds for each query half); COPY: issue the block copies.
+// visible (lane rows 4*hf + 8*(r/4) + r%4 of the block; the caller folds the
+// block's valid length, the row's own position and its member start into the
+// two per-lane thresholds); COPY: issue the block copies.
 template <int D, bool MASK, bool COPY>
-__device__ __forceinline__ void fwd_step(const Lanes16<D>& tl,
-                                         const BlockLoaderCM<D, kFwdWaves>& ldr,
+__device__ __forceinline__ void fwd_step(const LanesCM<D>& tl, const BlockLoaderCM<D, kFwdWaves>& ldr,
                                          const uint16_t* kt, const uint16_t* vt,
-                                         const bf16x8 (&qr)[2][D / 32], f32x4 (&acc)[D / 16][2],
-                                         float s2, bool first0, bool first1, float (&mu)[2],
-                                         float (&mlane)[2], float (&lsum)[2], uint32_t kdst,
-                                         i32x4 kdesc, uint32_t vdst, i32x4 vdesc, int hi0 = kBN,
-                                         int hi1 = kBN, int lo0 = 0, int lo1 = 0) {
-  constexpr int NF = D / 16;  // K fragments per block = V^T fragments per block
-  constexpr int PF = 2;       // LDS prefetch distance, in fragments
+                                         const bf16x8 (&qr)[D / 16], f32x16 (&acc)[D / 32],
+                                         float s2, bool first, float& mu, float& mlane,
+                                         float& lsum, uint32_t kdst, i32x4 kdesc, uint32_t vdst,
+                                         i32x4 vdesc, int hi = kBN, int lo = 0) {
+  constexpr int NS = D / 16;   // score MFMAs per step = PV MFMAs per step
+  constexpr int NMT = D / 32;  // 32-wide d tiles of O^T
+  constexpr int PF = 2;        // LDS prefetch distance, in MFMAs (3 spills in the loop)
   constexpr int NIW = BlockLoaderCM<D, kFwdWaves>::NIW;
-  constexpr int CEV = NF / (2 * NIW);
-  static_assert(CEV * 2 * NIW == NF, "copy instructions spread evenly over the PV fragments");
-  bf16x8 kf[NF], vf[NF];
+  constexpr int CEV = NS / (2 * NIW);  // PV segments per copy instruction
+  static_assert(CEV * 2 * NIW == NS, "copy instructions spread evenly over the PV MFMAs");
+  bf16x8 kf[NS], vf[NS];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) kf[i] = tl.krow(kt, i);
-  f32x4 s[2][2];
+  for (int i = 0; i < PF; ++i) kf[i] = tl.row8(kt, i);
+  f32x16 s;
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[kh][qh][r] = 0.f;
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  // the score MFMAs form one dependent chain; they win issue ties against the
+  // other wave's PV MFMAs (about 3 % faster than equal priorities)
   __builtin_amdgcn_s_setprio(2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    const int kk = i >> 1, kh = i & 1;
-    s[kh][0] = mfma16(kf[i], qr[0][kk], s[kh][0]);
-    s[kh][1] = mfma16(kf[i], qr[1][kk], s[kh][1]);
-    if (i + PF < NF) kf[i + PF] = tl.krow(kt, i + PF);
-    else vf[i + PF - NF] = tl.vcol(vt, i + PF - NF);
+  for (int i = 0; i < NS; ++i) {
+    s = mfma32(kf[i], qr[i], s);
+    if (i + PF < NS) {
+      kf[i + PF] = tl.row8(kt, i + PF);
+    } else {
+      const int j = i + PF - NS;
+      vf[j] = tl.col8(vt, j / NMT, j % NMT);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_setprio(0);
   if (MASK) {
+    // compile-time row offsets against the per-lane thresholds, so no key
+    // index is kept in a register
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+    for (int r = 0; r < 16; ++r) {
+      const int c = 8 * (r >> 2) + (r & 3);
+      s[r] = (c <= hi && c >= lo) ? s[r] : -kInf;
+    }
+  }
+  if (first) {
+    float mx = s[0];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 16 * kh + r;
-        s[kh][0][r] = (c <= hi0 && c >= lo0) ? s[kh][0][r] : -kInf;
-        s[kh][1][r] = (c <= hi1 && c >= lo1) ? s[kh][1][r] : -kInf;
-      }
-  }
-  if (first0) {
-    float mx = fmaxf(fmaxf(s[0][0][0], s[0][0][1]), fmaxf(s[0][0][2], s[0][0][3]));
-    mx = fmaxf(mx, fmaxf(fmaxf(s[1][0][0], s[1][0][1]), fmaxf(s[1][0][2], s[1][0][3])));
-    mu[0] = quad_max(mx) * s2;
-  }
-  if (first1) {
-    float mx = fmaxf(fmaxf(s[0][1][0], s[0][1][1]), fmaxf(s[0][1][2], s[0][1][3]));
-    mx = fmaxf(mx, fmaxf(fmaxf(s[1][1][0], s[1][1][1]), fmaxf(s[1][1][2], s[1][1][3])));
-    mu[1] = quad_max(mx) * s2;
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mu = wave_max_halves(mx) * s2;
   }
   bf16x8 pb[2];
+  float mx = mlane, ls = 0.f;
+  // a fully masked first block leaves no shift (masked blocks only)
+  const float mus = (MASK && mu == -kInf) ? 0.f : mu;
 #pragma unroll
-  for (int qh = 0; qh < 2; ++qh) {
-    float mx = mlane[qh], ls = 0.f;
-    const float mus = (MASK && mu[qh] == -kInf) ? 0.f : mu[qh];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = s[kh][qh][r];
-        mx = fmaxf(mx, x);
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, s2, -mus));
-        ls += p;
-        pb[qh][4 * kh + r] = to_bf16(p);
-      }
-    mlane[qh] = mx;
-    lsum[qh] += ls;
+  for (int r = 0; r < 16; ++r) {
+    const float x = s[r];
+    mx = fmaxf(mx, x);
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, s2, -mus));
+    ls += p;
+    pb[r >> 3][r & 7] = to_bf16(p);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    acc[j][0] = mfma16(vf[j], pb[0], acc[j][0]);
-    acc[j][1] = mfma16(vf[j], pb[1], acc[j][1]);
-    if (j + PF < NF) vf[j + PF] = tl.vcol(vt, j + PF);
+  for (int j = 0; j < NS; ++j) {
+    acc[j % NMT] = mfma32(vf[j], pb[j / NMT], acc[j % NMT]);
+    if (j + PF < NS) vf[j + PF] = tl.col8(vt, (j + PF) / NMT, (j + PF) % NMT);
     if (COPY && j % CEV == 0) ldr.issue(j / CEV, kdst, kdesc, vdst, vdesc);
     __builtin_amdgcn_sched_barrier(0);
   }
+  mlane = mx;
+  lsum += ls;
 }
 
 template <int D, bool RESP>
 __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
+  constexpr int NMT = D / 32;
   constexpr int TILE = kBN * D;                     // elements of one K or V block
   constexpr int NST = kStages;                      // ring depth (4)
   constexpr int NLD = 2 * BlockLoaderCM<D, kFwdWaves>::NIW;  // copy instructions per wave per block
@@ -155,7 +138,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   static_assert(NST == 4, "the ring has four stages");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = lane >> 4, n = lane & 15;
+  const int hf = lane >> 5, lq = lane & 31;
 
   const int w = RESP ? tile_item(a, kFwdRows, blockIdx.x, gridDim.x) : xcd_remap(blockIdx.x, gridDim.x);
   const int per_unit = a.mtiles * a.hkv;
@@ -165,7 +148,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   const int mtile = rem - kv * a.mtiles;
   const int GR = (a.hq / a.hkv) * a.R;
   const int m0 = mtile * kFwdRows;
-  const int mq[2] = {m0 + 32 * wave + n, m0 + 32 * wave + 16 + n};  // this lane's two query rows
+  const int m = m0 + 32 * wave + lq;     // this lane's query row within the group
   const size_t row0 = (size_t)kv * GR;
   const KeyWalk<D, RESP> walk(a, kv, unit, m0, kFwdRows);
   const int nblocks = walk.nblocks;
@@ -175,42 +158,35 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
   const int nfull = walk.nfull;
   const int slot = a.slot_base + unit;
 
-  // Q (B operand of query half qh): column = query mq[qh], k = 32*kk + 8G + e.
-  // Rows past the group are computed on a copy of its last row and never
-  // stored.  Masked blocks: the row sees response keys [member start, qoff +
-  // qi]; as thresholds relative to the lane's first key row 4G (keys past the
-  // block's valid rows lie beyond qoff + qi, so the bounds cover them).
-  bf16x8 qr[2][D / 32];
-  int lane_hi[2], lane_lo[2];
+  // Q (B operand): column = query m, k = 16*kk + 8*hf + e.  Rows past the
+  // group are computed on a copy of its last row and never stored.
+  bf16x8 qr[D / 16];
+  const int qi = m % a.R;
+  // masked blocks: the row sees response keys [member start, qoff + qi]; as
+  // thresholds relative to the lane's first key row 4*hf (keys past the
+  // block's valid rows lie beyond qoff + qi, so the bounds cover them)
+  const int lane_hi = RESP ? qi + a.qoff - 4 * hf : -4 * hf;
+  const int lane_lo = RESP ? member_start(a, qi) - 4 * hf : -4 * hf;
+  {
+    const uint16_t* qp = a.q + (row0 + min(m, GR - 1)) * D + 8 * hf;
 #pragma unroll
-  for (int qh = 0; qh < 2; ++qh) {
-    const int qi = mq[qh] % a.R;
-    lane_hi[qh] = RESP ? qi + a.qoff - 4 * G : -4 * G;
-    lane_lo[qh] = RESP ? member_start(a, qi) - 4 * G : -4 * G;
-    const uint16_t* qp = a.q + (row0 + min(mq[qh], GR - 1)) * D + 8 * G;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) qr[qh][kk] = ld_bf16x8(qp + 32 * kk);
+    for (int kk = 0; kk < D / 16; ++kk) qr[kk] = ld_bf16x8(qp + 16 * kk);
   }
-  Lanes16<D> tl(lane);
+  LanesCM<D> tl(hf, lq);
   const BlockLoaderCM<D, kFwdWaves> ldr(wave, lane);
 
-  f32x4 acc[D / 16][2];
-  float mref[2] = {-kInf, -kInf};   // exp2 shift of each query (log2 units)
-  float mtrue[2] = {-kInf, -kInf};  // running max of each query's scaled scores
-  float lsum[2] = {0.f, 0.f};
+  f32x16 acc[NMT];
+  float mref = -kInf;   // exp2 shift of this query (log2 units)
+  float mtrue = -kInf;  // running max of this query's scaled scores
+  float lsum = 0.f;
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[dt][qh][r] = 0.f;
-    lsum[0] = lsum[1] = 0.f;
-    if (pass == 1) {
-      mref[0] = mtrue[0];
-      mref[1] = mtrue[1];
-    }
+      for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+    lsum = 0.f;
+    if (pass == 1) mref = mtrue;
     bool unsafe = false;
     const bool pass0 = pass == 0;
 
@@ -246,12 +222,11 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
         load_block_cm<false>(ldr, kst[j], a.k + off, kBN);
         load_block_cm<true>(ldr, vst[j], a.v + off, kBN);
       }
-      float mlane[2] = {-kInf, -kInf};  // running max of this lane's raw scores in the range
+      float mlane = -kInf;  // running max of this lane's raw scores in the range
       // Values the loop reads that may have been reloaded from scratch: make
       // them resident here, so the loop body never waits on a pending reload
       // (such a wait would also drain the ring's copies).
-      asm volatile("" ::"v"(mref[0]), "v"(lsum[0]), "v"(mtrue[0]), "v"(mref[1]), "v"(lsum[1]),
-                   "v"(mtrue[1]));
+      asm volatile("" ::"v"(mref), "v"(lsum), "v"(mtrue));
 #define LS_FWD_STEP(ST)                                                                  \
   if (b + (ST) < nfull) {                                                                \
     /* K(b), V(b) landed; stage (ST+3)%4 (block b-1) is free */                         \
@@ -260,9 +235,8 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
     constexpr int SC = ((ST) + 3) % NST;                                                 \
     const size_t off = LS_BLOCK_OFF(b + (ST) + 3);                                       \
     /* pass 0 starts with no shift: its first block sets it */                          \
-    fwd_step<D, false, true>(tl, ldr, kst[ST], vst[ST], qr, acc, a.s2,                 \
-                pass0 && b + (ST) == 0, pass0 && b + (ST) == 0, mref, mlane, lsum,       \
-                lds_addr(kst[SC]),                                                       \
+    fwd_step<D, false, true>(tl, ldr, kst[ST], vst[ST], qr, acc, a.s2,                   \
+                pass0 && b + (ST) == 0, mref, mlane, lsum, lds_addr(kst[SC]),            \
                 block_desc(a.k + off, kBlkBytes), lds_addr(vst[SC]),                     \
                 block_desc(a.v + off, kBlkBytes));                                       \
   }
@@ -281,12 +255,9 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
       }
 #undef LS_FWD_STEP
 #undef LS_BLOCK_OFF
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        const float mb = quad_max(mlane[qh]) * a.s2;
-        mtrue[qh] = fmaxf(mtrue[qh], mb);
-        if (pass0) unsafe = unsafe || (mb > mref[qh] + kShiftSlack);
-      }
+      const float mb = wave_max_halves(mlane) * a.s2;
+      mtrue = fmaxf(mtrue, mb);
+      if (pass0) unsafe = unsafe || (mb > mref + kShiftSlack);
       wait_loads_le<0>();  // drain the look-ahead copies before LDS is reused
       __syncthreads();
     }
@@ -298,7 +269,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
     // block past the range gets a zero-length copy, which reads nothing and
     // is never computed), so "at most two blocks in flight" is a fixed vmcnt.
     {
-      float mlane[2] = {-kInf, -kInf};
+      float mlane = -kInf;
       int jb = max(nfull, walk.jfirst);
       // opaque per pass, so that the block addresses below are computed here
       // rather than hoisted out of the pass loop and kept live across it
@@ -307,7 +278,7 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
         // Q and any reloaded lane thresholds have landed: the compiler then
         // has no load of its own pending in the loop and adds no wait there
         // that would drain the copies
-        asm volatile("" ::"v"(lane_hi[0]), "v"(lane_lo[0]), "v"(lane_hi[1]), "v"(lane_lo[1]));
+        asm volatile("" ::"v"(lane_hi), "v"(lane_lo));
         wait_loads_le<0>();
 #define LS_ISSUE(J)                                                                       \
   {                                                                                       \
@@ -317,9 +288,9 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
     /* the clamp may be done on the vector unit: bring it back to a scalar */            \
     nv_ = __builtin_amdgcn_readfirstlane(max(nv_, 0));                                    \
     load_block_cm<false>(ldr, s_ == 0 ? k0 : s_ == 1 ? k1 : s_ == 2 ? k2 : k3, a.k + off_, \
-                           nv_);                                                          \
+                         nv_);                                                            \
     load_block_cm<true>(ldr, s_ == 0 ? v0 : s_ == 1 ? v1 : s_ == 2 ? v2 : v3, a.v + off_,  \
-                          nv_);                                                           \
+                        nv_);                                                             \
   }
         LS_ISSUE(jb)
         LS_ISSUE(jb + 1)
@@ -334,50 +305,45 @@ __global__ void __launch_bounds__(64 * kFwdWaves, 1) k_fwd(const AttnArgs a) {
             tl.refresh();
             const i32x4 none = {0, 0, 0, 0};
             fwd_step<D, true, false>(tl, ldr, s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3,
-                                       s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3, qr, acc,
-                                       a.s2, pass0 && mref[0] == -kInf, pass0 && mref[1] == -kInf,
-                                       mref, mlane, lsum, 0, none, 0, none,
-                                       RESP ? lane_hi[0] - key0 : lane_hi[0] + nv - 1,
-                                       RESP ? lane_hi[1] - key0 : lane_hi[1] + nv - 1,
-                                       lane_lo[0] - key0, lane_lo[1] - key0);
+                                     s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3, qr, acc,
+                                     a.s2, pass0 && mref == -kInf, mref, mlane, lsum, 0, none, 0,
+                                     none, RESP ? lane_hi - key0 : lane_hi + nv - 1,
+                                     lane_lo - key0);
           }
         }
 #undef LS_ISSUE
         wait_loads_le<0>();  // no copy into LDS outlives the loop
       }
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        const float mb = quad_max(mlane[qh]) * a.s2;
-        mtrue[qh] = fmaxf(mtrue[qh], mb);
-        if (pass0) unsafe = unsafe || (mb > mref[qh] + kShiftSlack);
-      }
+      const float mb = wave_max_halves(mlane) * a.s2;
+      mtrue = fmaxf(mtrue, mb);
+      if (pass0) unsafe = unsafe || (mb > mref + kShiftSlack);
     }
 
     if (!pass0 || !__syncthreads_or(unsafe ? 1 : 0)) break;
   }
 
   // ---- epilogue: o = O^T / l, m in natural-log units
-  const size_t rows_total = (size_t)a.hq * a.R;
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  if (m < GR) {
+    const size_t rows_total = (size_t)a.hq * a.R;
+    const size_t row = row0 + m;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float* op = a.o + ((size_t)slot * rows_total + row) * D + 4 * hf;
 #pragma unroll
-  for (int qh = 0; qh < 2; ++qh) {
-    const float lt = quad_sum(lsum[qh]);
-    if (mq[qh] < GR) {
-      const size_t row = row0 + mq[qh];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      float* op = a.o + ((size_t)slot * rows_total + row) * D + 4 * G;
+    for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
+      for (int r4 = 0; r4 < 4; ++r4) {
         float4 v;
-        v.x = acc[dt][qh][0] * inv;
-        v.y = acc[dt][qh][1] * inv;
-        v.z = acc[dt][qh][2] * inv;
-        v.w = acc[dt][qh][3] * inv;
-        *reinterpret_cast<float4*>(op + 16 * dt) = v;
+        v.x = acc[mt][4 * r4 + 0] * inv;
+        v.y = acc[mt][4 * r4 + 1] * inv;
+        v.z = acc[mt][4 * r4 + 2] * inv;
+        v.w = acc[mt][4 * r4 + 3] * inv;
+        *reinterpret_cast<float4*>(op + 32 * mt + 8 * r4) = v;
       }
-      if (G == 0) {
-        a.m[(size_t)slot * rows_total + row] = lt > 0.f ? mref[qh] * kLn2 : -kInf;
-        a.l[(size_t)slot * rows_total + row] = lt;
-      }
+    }
+    if (hf == 0) {
+      a.m[(size_t)slot * rows_total + row] = lt > 0.f ? mref * kLn2 : -kInf;
+      a.l[(size_t)slot * rows_total + row] = lt;
     }
   }
 }
